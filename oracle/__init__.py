@@ -1,0 +1,161 @@
+"""fp64 CPU oracle for exact attention: TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may import this
+package. The product library never loads it, and it shares no code with the GPU path.
+
+It follows the definition of attention on the page "FlashAttention 详解（零基础入门）"
+(§2.3 scores S = QK^T scaled, §2.4 safe softmax, §2.5 O = PV), the tiled algorithm of the
+same page (§5.2-§5.4 online softmax, §6.2 Q-outer / K,V-inner loop), the deferred
+normalisation of the narration script "FlashAttention 短片讲解稿" (segment 第二招 · 在线
+Softmax), and the causal mask and varlen packing of "FlashAttention 与算子融合" (fusion
+table, 工程实践). The arithmetic lives in oracle.cpp; this module converts the stored
+16-bit input bits to fp64 and calls it through ctypes.
+
+Every function here is pinned by tests/test_oracle_pins.py against values printed on the
+pages, closed forms, invariants, brute force and an autograd cross-check.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # ORACLE_LIB points the test suite at another build of oracle.cpp (the mutation
+        # test plants mistakes in copies of the source and checks that the pins fail).
+        path = os.environ.get("ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
+            _build.build()
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        L, D, I = ctypes.c_long, ctypes.c_double, ctypes.c_int
+        lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, D, I, I]
+        lib.oracle_fwd_blocked.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, D, I, L, L, I, dp, I]
+        lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, L, D, I, I]
+        lib.oracle_fwd_varlen.argtypes = [dp, dp, dp, dp, dp, ip, L, L, L, L, D, I, I]
+        lib.oracle_bwd_varlen.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ip, L, L, L, L,
+                                          D, I, I]
+        for f in ("oracle_fwd", "oracle_fwd_blocked", "oracle_bwd", "oracle_fwd_varlen",
+                  "oracle_bwd_varlen"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of stored 16-bit floats given as uint16 bit patterns.
+
+    bf16 is the upper half of an IEEE binary32; fp16 is IEEE binary16. Both widen to
+    binary64 without rounding.
+    """
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name} rejected its arguments (code {rc})")
+
+
+def fwd(q, k, v, scale, causal, nthreads=None):
+    """Plain definition. q, k, v: fp64 [B, N, H, d]. Returns (O [B,N,H,d], LSE [B,H,N])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, H, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    rc = _load().oracle_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, N, H, d, float(scale),
+                            int(bool(causal)), nthreads or default_threads())
+    _check(rc, "oracle_fwd")
+    return o, lse
+
+
+def fwd_blocked(q, k, v, scale, causal, block_q, block_k, form, nthreads=None):
+    """Tiled algorithm. form: "normalized" (guide §5.4 / §6.2) or "deferred" (narration).
+
+    Returns (O, LSE, trace) where trace[jb] = (m, l, state[0]) for row 0 of slice (0, 0)
+    after key block jb; state is O in the normalised form and the unnormalised numerator
+    in the deferred form.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, H, d = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    nkb = max(1, -(-N // block_k))
+    trace = np.full((nkb, 3), np.nan)
+    f = {"normalized": 0, "deferred": 1}[form]
+    rc = _load().oracle_fwd_blocked(_p(q), _p(k), _p(v), _p(o), _p(lse), B, N, H, d,
+                                    float(scale), int(bool(causal)), int(block_q), int(block_k),
+                                    f, _p(trace), nthreads or default_threads())
+    _check(rc, "oracle_fwd_blocked")
+    return o, lse, trace
+
+
+def bwd(q, k, v, o, lse, dout, scale, causal, nthreads=None):
+    """Gradients from the saved O and LSE. All [B,N,H,d] fp64 except lse [B,H,N]."""
+    q, k, v, o, lse, dout = map(_f64, (q, k, v, o, lse, dout))
+    B, N, H, d = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    rc = _load().oracle_bwd(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dout), _p(dq), _p(dk),
+                            _p(dv), B, N, H, d, float(scale), int(bool(causal)),
+                            nthreads or default_threads())
+    _check(rc, "oracle_bwd")
+    return dq, dk, dv
+
+
+def _cu(cu_seqlens):
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    return cu, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def fwd_varlen(q, k, v, cu_seqlens, scale, causal, nthreads=None):
+    """Packed sequences. q, k, v: fp64 [T, H, d]. Returns (O [T,H,d], LSE [H,T])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, H, d = q.shape
+    cu, cup = _cu(cu_seqlens)
+    o = np.zeros_like(q)
+    lse = np.full((H, T), np.nan)
+    rc = _load().oracle_fwd_varlen(_p(q), _p(k), _p(v), _p(o), _p(lse), cup, len(cu) - 1, T,
+                                   H, d, float(scale), int(bool(causal)),
+                                   nthreads or default_threads())
+    _check(rc, "oracle_fwd_varlen")
+    return o, lse
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, scale, causal, nthreads=None):
+    """Packed-sequence gradients; layouts as fwd_varlen."""
+    q, k, v, o, lse, dout = map(_f64, (q, k, v, o, lse, dout))
+    T, H, d = q.shape
+    cu, cup = _cu(cu_seqlens)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
+    rc = _load().oracle_bwd_varlen(_p(q), _p(k), _p(v), _p(o), _p(lse), _p(dout), _p(dq),
+                                   _p(dk), _p(dv), cup, len(cu) - 1, T, H, d, float(scale),
+                                   int(bool(causal)), nthreads or default_threads())
+    _check(rc, "oracle_bwd_varlen")
+    return dq, dk, dv

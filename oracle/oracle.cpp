@@ -1,0 +1,354 @@
+// Exact-attention oracle: plain fp64 CPU implementation of what the GPU path computes.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing in the product library links, loads or calls this
+// file; only the test suite, the smoke check and the benchmark's CPU-baseline leg do.
+// It shares no source, header, table or helper with the GPU kernels.
+//
+// What it computes (pages: "FlashAttention 详解（零基础入门）" §2.3-§2.6 for the
+// definition, §5.2-§5.4 and the §6.2 tiled algorithm for the blocked forms; the
+// narration script "FlashAttention 短片讲解稿", segment 第二招 · 在线 Softmax, for the
+// deferred-normalisation form; "FlashAttention 与算子融合" for the causal mask fused into
+// the kernel and for varlen packing):
+//
+//   s_ij  = scale * <q_i, k_j>                       (definition of S, §2.3)
+//   m_i   = max_{j in J(i)} s_ij                     (safe softmax, §2.4)
+//   l_i   = sum_{j in J(i)} exp(s_ij - m_i)
+//   O_i   = sum_{j in J(i)} exp(s_ij - m_i) v_j / l_i   (O = PV, §2.5)
+//   LSE_i = m_i + ln l_i                              (natural log)
+//
+// J(i) = {0..L-1} without a mask, {0..i} with the causal mask. A row with no visible key
+// (never produced by the supported inputs) is defined as O_i = 0, LSE_i = -inf.
+//
+// Backward: the pages state only that P is recomputed from Q, K, V, O and the saved row
+// statistics; the gradients are the chain rule through the definition above:
+//   P_ij = exp(s_ij - LSE_i), D_i = <dO_i, O_i>, dP_ij = <dO_i, v_j>,
+//   dS_ij = P_ij (dP_ij - D_i), dV_j = sum_i P_ij dO_i,
+//   dQ_i = scale sum_j dS_ij k_j, dK_j = scale sum_i dS_ij q_i.
+//
+// Layouts: q, k, v, o, dout, dq, dk, dv are [B, N, H, d] (d contiguous); lse is [B, H, N].
+// Varlen: the same with B = 1 and N = total tokens ([T, H, d], lse [H, T]); sequence s
+// occupies tokens [cu[s], cu[s+1]) and is an independent attention problem.
+//
+// Threads only split independent output rows (or heads); every sum is accumulated in
+// natural index order, so results do not depend on the thread count.
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <limits>
+#include <thread>
+#include <vector>
+
+namespace {
+
+const double kNegInf = -std::numeric_limits<double>::infinity();
+
+// One attention problem: a single (batch, head) or (sequence, head) slice.
+struct Slice {
+  const double* q;   // row i at q + i * rs
+  const double* k;
+  const double* v;
+  double* o;
+  double* lse;       // lse[i * ls]
+  long rs;           // row stride in elements (H * d)
+  long ls;           // lse stride (1)
+  long L;            // rows (= keys) in this slice
+};
+
+long visible_end(long i, long L, int causal) { return causal ? std::min(i + 1, L) : L; }
+
+double dot(const double* a, const double* b, long d) {
+  double s = 0.0;
+  for (long c = 0; c < d; ++c) s += a[c] * b[c];
+  return s;
+}
+
+// Run fn(item) for item in [0, n) on up to nthreads threads.
+template <class F>
+void parallel_for(long n, int nthreads, F fn) {
+  if (nthreads <= 1 || n <= 1) {
+    for (long i = 0; i < n; ++i) fn(i);
+    return;
+  }
+  std::atomic<long> next(0);
+  int nt = (int)std::min<long>(nthreads, n);
+  std::vector<std::thread> pool;
+  for (int t = 0; t < nt; ++t)
+    pool.emplace_back([&]() {
+      for (long i = next.fetch_add(1); i < n; i = next.fetch_add(1)) fn(i);
+    });
+  for (auto& th : pool) th.join();
+}
+
+// Plain definition, rows [r0, r1) of one slice.
+void fwd_rows(const Slice& s, long d, double scale, int causal, long r0, long r1) {
+  std::vector<double> sc(s.L);
+  for (long i = r0; i < r1; ++i) {
+    const long je = visible_end(i, s.L, causal);
+    const double* qi = s.q + i * s.rs;
+    double m = kNegInf;
+    for (long j = 0; j < je; ++j) {
+      sc[j] = scale * dot(qi, s.k + j * s.rs, d);
+      m = std::max(m, sc[j]);
+    }
+    double* oi = s.o + i * s.rs;
+    for (long c = 0; c < d; ++c) oi[c] = 0.0;
+    if (je == 0) {
+      s.lse[i * s.ls] = kNegInf;
+      continue;
+    }
+    double l = 0.0;
+    for (long j = 0; j < je; ++j) {
+      const double p = std::exp(sc[j] - m);
+      l += p;
+      const double* vj = s.v + j * s.rs;
+      for (long c = 0; c < d; ++c) oi[c] += p * vj[c];
+    }
+    for (long c = 0; c < d; ++c) oi[c] /= l;
+    s.lse[i * s.ls] = m + std::log(l);
+  }
+}
+
+// Tiled algorithm: query block [i0, i0+Bq) against every key block of size Bk, keeping a
+// running max m, running sum l and an output state per row (guide §5.4 and §6.2).
+//   form 0 (normalised): the state is O itself, re-normalised by l after every block.
+//   form 1 (deferred, as in the narration script): the state is the unnormalised
+//           numerator sum exp(s - m) v, divided by l once after the last block.
+// trace (nullable) receives, for row i0 only, one triple per key block:
+//   (m, l, state[0]) after that block.
+void fwd_block(const Slice& s, long d, double scale, int causal, long i0, long Bq, long Bk,
+               int form, double* trace) {
+  const long i1 = std::min(i0 + Bq, s.L);
+  const long nb = (s.L + Bk - 1) / Bk;
+  std::vector<double> m(i1 - i0, kNegInf), l(i1 - i0, 0.0), st((i1 - i0) * d, 0.0);
+  std::vector<double> sblk(Bk), p(Bk);
+  for (long jb = 0; jb < nb; ++jb) {
+    const long j0 = jb * Bk, j1 = std::min(j0 + Bk, s.L);
+    for (long i = i0; i < i1; ++i) {
+      const long r = i - i0;
+      const long je = std::min(j1, visible_end(i, s.L, causal));
+      double mb = kNegInf;
+      for (long j = j0; j < je; ++j) {
+        sblk[j - j0] = scale * dot(s.q + i * s.rs, s.k + j * s.rs, d);
+        mb = std::max(mb, sblk[j - j0]);
+      }
+      const double mn = std::max(m[r], mb);
+      if (mn != kNegInf) {  // otherwise no key of this row has been visible yet
+        const double alpha = std::exp(m[r] - mn);  // exp(-inf) = 0 on the first block
+        double rowsum = 0.0;
+        for (long j = j0; j < je; ++j) {
+          p[j - j0] = std::exp(sblk[j - j0] - mn);
+          rowsum += p[j - j0];
+        }
+        const double ln = l[r] * alpha + rowsum;
+        double* sr = st.data() + r * d;
+        for (long c = 0; c < d; ++c) {
+          double pv = 0.0;
+          for (long j = j0; j < je; ++j) pv += p[j - j0] * s.v[j * s.rs + c];
+          if (form == 0)
+            sr[c] = sr[c] * (l[r] / ln) * alpha + pv / ln;
+          else
+            sr[c] = sr[c] * alpha + pv;
+        }
+        m[r] = mn;
+        l[r] = ln;
+      }
+      if (trace && i == i0) {
+        trace[3 * jb + 0] = m[r];
+        trace[3 * jb + 1] = l[r];
+        trace[3 * jb + 2] = st[r * d];
+      }
+    }
+  }
+  for (long i = i0; i < i1; ++i) {
+    const long r = i - i0;
+    double* oi = s.o + i * s.rs;
+    for (long c = 0; c < d; ++c) {
+      if (l[r] == 0.0)
+        oi[c] = 0.0;
+      else
+        oi[c] = form == 0 ? st[r * d + c] : st[r * d + c] / l[r];
+    }
+    s.lse[i * s.ls] = l[r] == 0.0 ? kNegInf : m[r] + std::log(l[r]);
+  }
+}
+
+struct GradSlice {
+  Slice f;
+  const double* dout;
+  double* dq;
+  double* dk;
+  double* dv;
+};
+
+// dQ for rows [r0, r1): dQ_i = scale * sum_j P_ij (dP_ij - D_i) k_j.
+void bwd_dq_rows(const GradSlice& g, long d, double scale, int causal, long r0, long r1) {
+  const Slice& s = g.f;
+  for (long i = r0; i < r1; ++i) {
+    const long je = visible_end(i, s.L, causal);
+    const double* qi = s.q + i * s.rs;
+    const double* doi = g.dout + i * s.rs;
+    const double Di = dot(doi, s.o + i * s.rs, d);
+    const double lse = s.lse[i * s.ls];
+    double* dqi = g.dq + i * s.rs;
+    for (long c = 0; c < d; ++c) dqi[c] = 0.0;
+    for (long j = 0; j < je; ++j) {
+      const double P = std::exp(scale * dot(qi, s.k + j * s.rs, d) - lse);
+      const double dP = dot(doi, s.v + j * s.rs, d);
+      const double dS = P * (dP - Di);
+      const double* kj = s.k + j * s.rs;
+      for (long c = 0; c < d; ++c) dqi[c] += dS * kj[c];
+    }
+    for (long c = 0; c < d; ++c) dqi[c] *= scale;
+  }
+}
+
+// dK, dV for key rows [c0, c1): dV_j = sum_i P_ij dO_i, dK_j = scale * sum_i dS_ij q_i,
+// over the query rows i that see key j.
+void bwd_dkdv_rows(const GradSlice& g, long d, double scale, int causal, long c0, long c1) {
+  const Slice& s = g.f;
+  for (long j = c0; j < c1; ++j) {
+    const double* kj = s.k + j * s.rs;
+    const double* vj = s.v + j * s.rs;
+    double* dkj = g.dk + j * s.rs;
+    double* dvj = g.dv + j * s.rs;
+    for (long c = 0; c < d; ++c) dkj[c] = dvj[c] = 0.0;
+    for (long i = causal ? j : 0; i < s.L; ++i) {
+      const double* qi = s.q + i * s.rs;
+      const double* doi = g.dout + i * s.rs;
+      const double Di = dot(doi, s.o + i * s.rs, d);
+      const double P = std::exp(scale * dot(qi, kj, d) - s.lse[i * s.ls]);
+      const double dP = dot(doi, vj, d);
+      const double dS = P * (dP - Di);
+      for (long c = 0; c < d; ++c) {
+        dvj[c] += P * doi[c];
+        dkj[c] += dS * qi[c];
+      }
+    }
+    for (long c = 0; c < d; ++c) dkj[c] *= scale;
+  }
+}
+
+const long kRowChunk = 32;
+
+bool bad_sizes(long B, long N, long H, long d) { return B < 0 || N < 0 || H <= 0 || d <= 0; }
+
+// Slices of a dense [B, N, H, d] problem: slice index = b * H + h.
+Slice dense_slice(const double* q, const double* k, const double* v, double* o, double* lse,
+                  long N, long H, long d, long idx) {
+  const long b = idx / H, h = idx % H;
+  const long off = b * N * H * d + h * d;
+  return Slice{q + off, k + off, v + off, o + off, lse + (b * H + h) * N, H * d, 1, N};
+}
+
+}  // namespace
+
+extern "C" {
+
+// Plain definition (O1-O4). Returns 0, or -1 on bad sizes.
+int oracle_fwd(const double* q, const double* k, const double* v, double* o, double* lse,
+               long B, long N, long H, long d, double scale, int causal, int nthreads) {
+  if (bad_sizes(B, N, H, d)) return -1;
+  const long chunks = (N + kRowChunk - 1) / kRowChunk;
+  parallel_for(B * H * chunks, nthreads, [&](long it) {
+    Slice s = dense_slice(q, k, v, o, lse, N, H, d, it / chunks);
+    const long r0 = (it % chunks) * kRowChunk;
+    fwd_rows(s, d, scale, causal, r0, std::min(r0 + kRowChunk, N));
+  });
+  return 0;
+}
+
+// Tiled algorithm with query blocks of Bq rows and key blocks of Bk rows (any sizes >= 1,
+// divisors of N or not). form: 0 normalised update, 1 deferred normalisation.
+// trace (nullable) gets (m, l, state[0]) after each key block for row 0 of slice (0, 0):
+// 3 * ceil(N / Bk) doubles.
+int oracle_fwd_blocked(const double* q, const double* k, const double* v, double* o,
+                       double* lse, long B, long N, long H, long d, double scale, int causal,
+                       long Bq, long Bk, int form, double* trace, int nthreads) {
+  if (bad_sizes(B, N, H, d) || Bq < 1 || Bk < 1 || (form != 0 && form != 1)) return -1;
+  const long qblocks = (N + Bq - 1) / Bq;
+  parallel_for(B * H * qblocks, nthreads, [&](long it) {
+    const long idx = it / qblocks, ib = it % qblocks;
+    Slice s = dense_slice(q, k, v, o, lse, N, H, d, idx);
+    fwd_block(s, d, scale, causal, ib * Bq, Bq, Bk, form, (idx == 0 && ib == 0) ? trace : nullptr);
+  });
+  return 0;
+}
+
+// Gradients from the saved O and LSE (B1-B4 of the chain rule above).
+int oracle_bwd(const double* q, const double* k, const double* v, const double* o,
+               const double* lse, const double* dout, double* dq, double* dk, double* dv,
+               long B, long N, long H, long d, double scale, int causal, int nthreads) {
+  if (bad_sizes(B, N, H, d)) return -1;
+  const long chunks = (N + kRowChunk - 1) / kRowChunk;
+  auto grad_slice = [&](long idx) {
+    const long b = idx / H, h = idx % H;
+    const long off = b * N * H * d + h * d;
+    GradSlice g{Slice{q + off, k + off, v + off, const_cast<double*>(o + off),
+                      const_cast<double*>(lse + (b * H + h) * N), H * d, 1, N},
+                dout + off, dq + off, dk + off, dv + off};
+    return g;
+  };
+  parallel_for(B * H * chunks, nthreads, [&](long it) {
+    GradSlice g = grad_slice(it / chunks);
+    const long r0 = (it % chunks) * kRowChunk;
+    bwd_dq_rows(g, d, scale, causal, r0, std::min(r0 + kRowChunk, N));
+  });
+  parallel_for(B * H * chunks, nthreads, [&](long it) {
+    GradSlice g = grad_slice(it / chunks);
+    const long c0 = (it % chunks) * kRowChunk;
+    bwd_dkdv_rows(g, d, scale, causal, c0, std::min(c0 + kRowChunk, N));
+  });
+  return 0;
+}
+
+// Packed sequences: q, k, v, o [T, H, d]; lse [H, T]; cu_seqlens int32 [nseq + 1].
+// Returns -2 if cu_seqlens is not a valid prefix-sum array (cu[0] = 0, non-decreasing,
+// cu[nseq] = T).
+int oracle_fwd_varlen(const double* q, const double* k, const double* v, double* o,
+                      double* lse, const int32_t* cu, long nseq, long T, long H, long d,
+                      double scale, int causal, int nthreads) {
+  if (nseq < 0 || T < 0 || H <= 0 || d <= 0) return -1;
+  if (cu[0] != 0 || cu[nseq] != T) return -2;
+  for (long s = 0; s < nseq; ++s)
+    if (cu[s + 1] < cu[s]) return -2;
+  // work items: (sequence, head, row chunk)
+  std::vector<long> first(nseq + 1, 0);
+  for (long s = 0; s < nseq; ++s)
+    first[s + 1] = first[s] + H * ((cu[s + 1] - cu[s] + kRowChunk - 1) / kRowChunk);
+  parallel_for(first[nseq], nthreads, [&](long it) {
+    const long s = std::upper_bound(first.begin(), first.end(), it) - first.begin() - 1;
+    const long L = cu[s + 1] - cu[s];
+    const long chunks = (L + kRowChunk - 1) / kRowChunk;
+    const long h = (it - first[s]) / chunks, r0 = ((it - first[s]) % chunks) * kRowChunk;
+    const long off = (long)cu[s] * H * d + h * d;
+    Slice sl{q + off, k + off, v + off, o + off, lse + h * T + cu[s], H * d, 1, L};
+    fwd_rows(sl, d, scale, causal, r0, std::min(r0 + kRowChunk, L));
+  });
+  return 0;
+}
+
+// Packed-sequence gradients (same layouts as oracle_fwd_varlen; dout, dq, dk, dv [T, H, d]).
+int oracle_bwd_varlen(const double* q, const double* k, const double* v, const double* o,
+                      const double* lse, const double* dout, double* dq, double* dk,
+                      double* dv, const int32_t* cu, long nseq, long T, long H, long d,
+                      double scale, int causal, int nthreads) {
+  if (nseq < 0 || T < 0 || H <= 0 || d <= 0) return -1;
+  if (cu[0] != 0 || cu[nseq] != T) return -2;
+  for (long s = 0; s < nseq; ++s)
+    if (cu[s + 1] < cu[s]) return -2;
+  parallel_for(nseq * H, nthreads, [&](long it) {
+    const long s = it / H, h = it % H;
+    const long L = cu[s + 1] - cu[s];
+    const long off = (long)cu[s] * H * d + h * d;
+    GradSlice g{Slice{q + off, k + off, v + off, const_cast<double*>(o + off),
+                      const_cast<double*>(lse + h * T + cu[s]), H * d, 1, L},
+                dout + off, dq + off, dk + off, dv + off};
+    bwd_dq_rows(g, d, scale, causal, 0, L);
+    bwd_dkdv_rows(g, d, scale, causal, 0, L);
+  });
+  return 0;
+}
+
+}  // extern "C"
