@@ -1,0 +1,167 @@
+"""Python binding of libfa_mi355x.so, the gfx950 exact-attention library (include/fa.h).
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels. PyTorch supplies device memory (outputs are allocated with torch.empty) and the
+current HIP stream. There is no fallback: if the library is missing the calls raise.
+
+    o, lse = fa_fwd(q, k, v, causal=False, softmax_scale=None)
+    dq, dk, dv = fa_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None)
+    o, lse = fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, softmax_scale=None)
+
+q, k, v, o, dout: [B, N, H, d] (packed: [T, H, d]) contiguous bf16 or fp16 CUDA tensors;
+lse: fp32 [B, H, N] (packed: [H, T]); d in {64, 128}; softmax_scale defaults to 1/sqrt(d).
+"""
+import ctypes
+import math
+import os
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_varlen", "fa_bwd_workspace_size", "fa_status_string",
+           "FAError", "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libfa_mi355x.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F16, FA_BF16 = 0, 1
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {fa_status_string(code)} (status {code})")
+        self.code = code
+
+
+def load_library():
+    """Load the built library (ctypes). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing; build it with `python -m exact_io_aware_10_amd.build`")
+    lib = ctypes.CDLL(library_path)
+    vp, i, f, s = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = s
+    lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp] * 6 + [i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_varlen.restype = i
+    _lib = lib
+    return lib
+
+
+def fa_status_string(code: int) -> str:
+    return load_library().fa_status_string(int(code)).decode()
+
+
+def fa_bwd_workspace_size(B: int, N: int, H: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, N, H, d))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_F16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float16")
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def _scale(softmax_scale, d):
+    return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+
+
+def fa_fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None):
+    """Forward attention. Returns (o [B,N,H,d], lse fp32 [B,H,N])."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N, H, d]")
+    B, N, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("out", o, q.shape, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, H, N), torch.float32, q.device)
+    rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    B, N, H, d, _dtype_code(q), _scale(softmax_scale, d), int(bool(causal)),
+                    _stream(q.device))
+    if rc != FA_OK:
+        raise FAError("fa_fwd", rc)
+    return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, workspace=None):
+    """Backward attention from the forward's o and lse. Returns (dq, dk, dv)."""
+    torch = _torch()
+    lib = load_library()
+    B, N, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, H, N), torch.float32, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    nbytes = fa_bwd_workspace_size(B, N, H, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    workspace.data_ptr(), B, N, H, d, _dtype_code(q), _scale(softmax_scale, d),
+                    int(bool(causal)), _stream(q.device))
+    if rc != FA_OK:
+        raise FAError("fa_bwd", rc)
+    return dq, dk, dv
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, softmax_scale=None):
+    """Packed-sequence forward. q, k, v: [T, H, d]; cu_seqlens: int32 CUDA [nseq + 1].
+    Returns (o [T,H,d], lse fp32 [H,T])."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d]")
+    T, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    rc = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T,
+                           int(max_seqlen), H, d, _dtype_code(q), _scale(softmax_scale, d),
+                           int(bool(causal)), _stream(q.device))
+    if rc != FA_OK:
+        raise FAError("fa_fwd_varlen", rc)
+    return o, lse

@@ -1,0 +1,139 @@
+// C-ABI entry points of libfa_mi355x.so: synchronous argument checks, then kernel
+// launches on the caller's stream. Declarations and contracts: include/fa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+#define FA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+// (N + 256) * H * d limit: byte offsets of every row a kernel touches, including the
+// padded rows of a ragged last tile, fit in 31 bits.
+constexpr long kMaxSliceElems = 1L << 30;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dtype_ok(fa_dtype dt) { return dt == FA_F16 || dt == FA_BF16; }
+
+fa_status to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// Shared checks of the scalar arguments. Returns FA_OK when the request is valid.
+fa_status check_common(long B, long N, long H, int d, fa_dtype dt, float scale) {
+  if (B < 0 || N < 0 || H < 0) return FA_ERR_INVALID_ARG;
+  if (!dtype_ok(dt) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((N + 256) * H * d >= kMaxSliceElems) return FA_ERR_UNSUPPORTED;
+  if (B * H * ((N + 127) / 128) >= (1L << 31)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+bool tensors_ok(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr || !aligned16(p)) return false;
+  return true;
+}
+
+}  // namespace
+
+FA_EXPORT const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+FA_EXPORT fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int N, int H, int d, fa_dtype dtype, float softmax_scale,
+                           int causal, hipStream_t stream) {
+  fa_status st = check_common(B, N, H, d, dtype, softmax_scale);
+  if (st != FA_OK) return st;
+  if ((long)B * N * H == 0) return FA_OK;
+  if (!tensors_ok({q, k, v, o}) || lse == nullptr || ((uintptr_t)lse & 3u))
+    return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.cu = nullptr;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.T = B * N;
+  a.scale_log2 = fabsf(softmax_scale) * kLog2e;
+  a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
+  return to_status(fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, false, stream));
+}
+
+FA_EXPORT size_t fa_bwd_workspace_size(int B, int N, int H, int d) {
+  if (B < 0 || N < 0 || H < 0 || (d != 64 && d != 128)) return 0;
+  return (size_t)4 * B * H * N;
+}
+
+FA_EXPORT fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                           float softmax_scale, int causal, hipStream_t stream) {
+  fa_status st = check_common(B, N, H, d, dtype, softmax_scale);
+  if (st != FA_OK) return st;
+  if ((long)B * N * H == 0) return FA_OK;
+  if (!tensors_ok({q, k, v, o, dout, dq, dk, dv, workspace}) || lse == nullptr ||
+      ((uintptr_t)lse & 3u))
+    return FA_ERR_INVALID_ARG;
+  fa::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.delta = static_cast<float*>(workspace);
+  a.cu = nullptr;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.T = B * N;
+  a.scale = softmax_scale;
+  a.scale_log2 = fabsf(softmax_scale) * kLog2e;
+  a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
+  return to_status(fa::launch_bwd(a, d, dtype == FA_BF16, causal != 0, false, stream));
+}
+
+FA_EXPORT fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int32_t* cu_seqlens, int num_seqs,
+                                  int total_tokens, int max_seqlen, int H, int d,
+                                  fa_dtype dtype, float softmax_scale, int causal,
+                                  hipStream_t stream) {
+  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0) return FA_ERR_INVALID_ARG;
+  fa_status st = check_common(num_seqs, max_seqlen, H, d, dtype, softmax_scale);
+  if (st != FA_OK) return st;
+  if (cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3u)) return FA_ERR_INVALID_ARG;
+  if ((long)num_seqs * max_seqlen * H == 0 || total_tokens == 0) return FA_OK;
+  if (!tensors_ok({q, k, v, o}) || lse == nullptr || ((uintptr_t)lse & 3u))
+    return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.cu = cu_seqlens;
+  a.B = num_seqs;
+  a.N = max_seqlen;
+  a.H = H;
+  a.T = total_tokens;
+  a.scale_log2 = fabsf(softmax_scale) * kLog2e;
+  a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
+  return to_status(fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, true, stream));
+}

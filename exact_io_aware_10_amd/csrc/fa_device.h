@@ -1,0 +1,114 @@
+// Device-side building blocks for the gfx950 attention kernels: operand vector types,
+// bf16/fp16 MFMA wrappers, buffer-resource loads with hardware bounds checks, exp2/log2,
+// RNE conversions and the XCD-aware work remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Element type tags. Both are 16-bit storage; the tag picks the MFMA and the rounding.
+struct BF16 {};
+struct F16 {};
+
+// C[32x32] += A[32x16] * B[16x32] with fp32 accumulation (v_mfma_f32_32x32x16_{bf16,f16}).
+// Operand layout (lane l, g = l / 32): A holds A[l % 32][8g .. 8g+7], B holds
+// B[8g .. 8g+7][l % 32]; C register r of lane l is C[8(r/4) + 4g + r%4][l % 32].
+template <class T>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<BF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 values -> packed 16-bit pair, round to nearest even (low half = x).
+template <class T>
+__device__ __forceinline__ uint32_t pack2(float x, float y);
+template <>
+__device__ __forceinline__ uint32_t pack2<BF16>(float x, float y) {
+  f32x2 v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<F16>(float x, float y) {
+  f32x2 v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// 16-bit element -> fp32 (exact).
+template <class T>
+__device__ __forceinline__ float to_f32(uint32_t bits16);
+template <>
+__device__ __forceinline__ float to_f32<BF16>(uint32_t b) { return __uint_as_float(b << 16); }
+template <>
+__device__ __forceinline__ float to_f32<F16>(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+__device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2f_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// Buffer resource over [base, base + nbytes): loads past nbytes return 0 and stores past
+// it are dropped, so ragged tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+
+// Row reductions across the lane pair (l, l ^ 32). v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second; with both operands = x the
+// two results hold, per lane, x and the partner's x (in an order that depends on the half),
+// so a symmetric combination of the two is the pair's reduction in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (XCD = linear id % 8), each with
+// its own L2. Remap the linear id so that XCD x receives a contiguous range of logical
+// work items; neighbouring items (query blocks of one head) then share that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t lin, uint32_t total) {
+  const uint32_t nx = 8;
+  const uint32_t q = total / nx, r = total % nx;
+  const uint32_t x = lin % nx, slot = lin / nx;
+  return x * q + (x < r ? x : r) + slot;
+}
+
+}  // namespace fa

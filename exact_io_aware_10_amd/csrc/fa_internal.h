@@ -1,0 +1,49 @@
+// Internal (non-exported) interface between the C-ABI entry points and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// One forward launch. Dense: B batches of N tokens. Varlen: B = number of sequences,
+// N = max_seqlen, T = total tokens, cu = device cu_seqlens.
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int32_t* cu;
+  int B, N, H, T;
+  float scale_log2;  // |softmax_scale| * log2(e)
+  uint32_t qsign;    // 0x80008000 flips the sign of q (negative softmax_scale), else 0
+};
+
+// One backward launch (dense or varlen, same conventions as FwdArgs).
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;  // workspace: D_i = <dO_i, O_i>, fp32, same layout as lse
+  const int32_t* cu;
+  int B, N, H, T;
+  float scale;       // softmax_scale (signed)
+  float scale_log2;  // |softmax_scale| * log2(e)
+  uint32_t qsign;
+};
+
+__attribute__((visibility("hidden"))) hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16,
+                                                            bool causal, bool varlen,
+                                                            hipStream_t stream);
+__attribute__((visibility("hidden"))) hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16,
+                                                            bool causal, bool varlen,
+                                                            hipStream_t stream);
+
+}  // namespace fa

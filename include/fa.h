@@ -1,0 +1,124 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention library (libfa_mi355x.so).
+ *
+ * The library computes exact attention O = softmax(scale * Q K^T) V, tiled so that the
+ * N x N score matrix S and probability matrix P exist only as on-chip tiles and are never
+ * written to device memory. Definitions: "FlashAttention 详解（零基础入门）"
+ * (https://blog-dist-2hw.pages.dev/2026/07/19/flashattention-guide/) §2.3-§2.6 for
+ * S = Q K^T / sqrt(d), P = softmax(S), O = P V, §2.4 for the max-subtracted softmax, §5-§6
+ * for online softmax and the tiled loop; "FlashAttention 短片讲解稿"
+ * (https://xuujii.github.io/ai-infra-kb/videos/flashattention/讲解稿.md), segment 第三招 ·
+ * 反向重计算, for the backward pass that recomputes P tiles from the inputs, the output and
+ * per-row statistics; "FlashAttention 与算子融合"
+ * (https://ai-infra-wiki.pages.dev/compilers-kernels/02-kernels/flash-attention/), fusion
+ * table (mask fused into the kernel) and 工程实践 (varlen packing instead of padding).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library allocates
+ *    nothing, keeps no global state, never synchronises, and enqueues its kernels on
+ *    `stream` (a hipStream_t; NULL means the default stream). Calls on different streams
+ *    may run concurrently.
+ *  - Layout: q, k, v, o, dout, dq, dk, dv are [B, N, H, d] row-major (d contiguous, then
+ *    heads, then tokens, then batch), 16-byte aligned. lse is fp32 [B, H, N].
+ *    Packed (varlen) tensors are [T, H, d] with lse fp32 [H, T].
+ *  - Element type: dtype FA_BF16 or FA_F16 for q, k, v, o, dout, dq, dk, dv. Products
+ *    accumulate in fp32; P is rounded to the element type (nearest even) before P V.
+ *  - head dim d must be 64 or 128.
+ *  - softmax_scale multiplies the scores before the softmax; pass 1/sqrt(d) for the
+ *    usual attention. Any finite value is accepted.
+ *  - causal != 0 masks key j for query i when j > i (positions within the sequence).
+ *  - lse[i] = m_i + ln(l_i), the natural-log log-sum-exp of row i's scaled, masked scores.
+ *  - Errors: argument checks are synchronous and return a status without launching
+ *    anything. FA_ERR_HIP reports a launch failure (hipGetLastError after the launch);
+ *    faults inside a kernel surface at the caller's next synchronisation, as for any
+ *    stream work.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, negative size, non-finite scale, bad layout */
+  FA_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels handle (head dim, sizes) */
+  FA_ERR_HIP = 3          /* a HIP launch reported an error */
+} fa_status;
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Short static description of a status code. Never NULL. */
+const char* fa_status_string(fa_status s);
+
+/*
+ * Forward pass (guide §6.2 tiled algorithm; narration 第二招 for the deferred
+ * normalisation): for each (b, h), O = softmax(scale * Q K^T [+ causal mask]) V and the
+ * per-row log-sum-exp.
+ *   q, k, v : in,  [B, N, H, d], dtype
+ *   o       : out, [B, N, H, d], dtype
+ *   lse     : out, fp32 [B, H, N]
+ * B, N, H >= 0 (B*N*H == 0 is a no-op returning FA_OK). Limit: (N + 256) * H * d < 2^30.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int N, int H, int d, fa_dtype dtype, float softmax_scale, int causal,
+                 hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: 4 * B * H * N (the fp32 row terms
+ * D_i = <dO_i, O_i>). Linear in N: the backward never stores an N x N matrix.
+ */
+size_t fa_bwd_workspace_size(int B, int N, int H, int d);
+
+/*
+ * Backward pass (narration 第三招 · 反向重计算: P is recomputed tile by tile from q, k and
+ * the forward's lse instead of being stored). Gradients of the loss through O:
+ *   P_ij = exp(scale <q_i,k_j> - lse_i), D_i = <dO_i, O_i>, dV_j = sum_i P_ij dO_i,
+ *   dS_ij = P_ij (<dO_i, v_j> - D_i), dQ_i = scale sum_j dS_ij k_j,
+ *   dK_j = scale sum_i dS_ij q_i.
+ *   q, k, v, o, dout : in,  [B, N, H, d], dtype (o and lse from fa_fwd with the same
+ *                      scale and causal flag)
+ *   lse              : in,  fp32 [B, H, N]
+ *   dq, dk, dv       : out, [B, N, H, d], dtype
+ *   workspace        : scratch of fa_bwd_workspace_size(B, N, H, d) bytes, 16-byte
+ *                      aligned; its contents are overwritten. May be NULL if that size is 0.
+ * Deterministic: no floating-point atomics; repeated calls give identical bits.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                 void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                 float softmax_scale, int causal, hipStream_t stream);
+
+/*
+ * Forward pass over packed sequences (fusion page, 工程实践: pack unequal lengths instead
+ * of padding). Sequence s occupies tokens [cu_seqlens[s], cu_seqlens[s+1]) of the packed
+ * tensors and is an independent attention problem; the causal mask is relative to the
+ * start of each sequence.
+ *   q, k, v     : in,  [total_tokens, H, d], dtype
+ *   o           : out, [total_tokens, H, d], dtype
+ *   lse         : out, fp32 [H, total_tokens]
+ *   cu_seqlens  : in,  device int32 [num_seqs + 1], cu[0] = 0, non-decreasing,
+ *                 cu[num_seqs] = total_tokens
+ *   max_seqlen  : host-side upper bound on the sequence lengths (sizes the grid without a
+ *                 device-to-host copy); lengths above it are not processed.
+ * Limit: (max_seqlen + 256) * H * d < 2^30. Sequences longer than max_seqlen are treated
+ * as truncated to max_seqlen tokens (their later rows are not written). A malformed cu_seqlens gives undefined results
+ * (out-of-range rows are clamped by hardware bounds checks, never read or written outside
+ * the packed tensors).
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens, int num_seqs, int total_tokens,
+                        int max_seqlen, int H, int d, fa_dtype dtype, float softmax_scale,
+                        int causal, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -50,10 +50,12 @@ def _load():
 
 
 def default_threads() -> int:
+    """Host threads for the oracle: the cores this process may run on, at most 16."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 def widen(bits: np.ndarray, dtype: str) -> np.ndarray:

@@ -1,0 +1,105 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function include/fa.h
+declares, and rejects bad arguments synchronously (no GPU is touched by these calls)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_io_aware_10_amd as fa
+    return fa.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_fwd_varlen"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    import exact_io_aware_10_amd as fa
+    assert fa.fa_status_string(0) == "ok"
+    assert fa.fa_status_string(1) == "invalid argument"
+    assert fa.fa_status_string(2) == "unsupported configuration"
+    assert fa.fa_status_string(3) == "HIP launch error"
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+FAKE = 1 << 20  # a 16-byte aligned, never dereferenced address (checks fail before launch)
+
+
+def call_fwd(lib, q=FAKE, lse=FAKE, B=1, N=8, H=1, d=64, dt=1, scale=0.125, causal=0):
+    return lib.fa_fwd(q, FAKE, FAKE, FAKE, lse, B, N, H, d, dt, ctypes.c_float(scale), causal,
+                      None)
+
+
+def test_fwd_argument_checks(lib):
+    assert call_fwd(lib, q=None) == 1
+    assert call_fwd(lib, q=FAKE + 2) == 1          # misaligned
+    assert call_fwd(lib, lse=None) == 1
+    assert call_fwd(lib, B=-1) == 1
+    assert call_fwd(lib, dt=7) == 1
+    assert call_fwd(lib, scale=float("nan")) == 1
+    assert call_fwd(lib, scale=float("inf")) == 1
+    assert call_fwd(lib, d=96) == 2
+    assert call_fwd(lib, d=256) == 2
+    assert call_fwd(lib, N=1 << 20, H=64, d=128) == 2   # N*H*d beyond the offset range
+    assert call_fwd(lib, B=0) == 0                    # empty problem: nothing to do
+    assert call_fwd(lib, q=None, N=0) == 0
+
+
+def test_bwd_argument_checks(lib):
+    args = [FAKE] * 10
+    f = ctypes.c_float(0.1)
+    bad = list(args)
+    bad[9] = None  # workspace
+    assert lib.fa_bwd(*bad, 1, 8, 1, 64, 1, f, 0, None) == 1
+    bad = list(args)
+    bad[0] = None
+    assert lib.fa_bwd(*bad, 1, 8, 1, 64, 1, f, 0, None) == 1
+    assert lib.fa_bwd(*args, 1, 8, 1, 80, 1, f, 0, None) == 2
+    assert lib.fa_bwd(*args, 0, 8, 1, 64, 1, f, 0, None) == 0
+
+
+def test_varlen_argument_checks(lib):
+    f = ctypes.c_float(0.1)
+    a = [FAKE] * 5
+    assert lib.fa_fwd_varlen(*a, None, 2, 100, 64, 2, 64, 1, f, 1, None) == 1   # no cu_seqlens
+    assert lib.fa_fwd_varlen(*a, FAKE, -1, 100, 64, 2, 64, 1, f, 1, None) == 1
+    assert lib.fa_fwd_varlen(*a, FAKE, 2, 100, 64, 2, 72, 1, f, 1, None) == 2
+    assert lib.fa_fwd_varlen(*a, FAKE, 2, 0, 64, 2, 64, 1, f, 1, None) == 0
+
+
+def test_workspace_is_linear_in_sequence_length(lib):
+    """The backward's scratch grows like B*H*N, never N^2: compare it against the size of
+    one head's full fp16 score matrix that the guide tabulates (§3.1)."""
+    import exact_io_aware_10_amd as fa
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "guide_score_matrix_sizes.json"),
+                       encoding="utf-8"))
+    unit = {"MB": 2 ** 20, "GB": 2 ** 30}
+    for row in g["rows"]:
+        n = row["N"]
+        s_bytes = row["size"] * unit[row["unit"]]
+        assert s_bytes == n * n * g["bytes_per_element"]  # the table is the N*N*2 closed form
+        ws = fa.fa_bwd_workspace_size(1, n, 1, 128)
+        assert ws == 4 * n
+        assert ws * 1024 <= s_bytes or n < 4096
+    assert fa.fa_bwd_workspace_size(4, 4096, 16, 128) == 4 * 4 * 16 * 4096
+    assert fa.fa_bwd_workspace_size(1, 8, 1, 96) == 0
