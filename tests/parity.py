@@ -5,7 +5,13 @@ Tolerances (per tensor, against the fp64 oracle on the same stored inputs): max-
 <= 2e-2 and mean-abs error <= 2e-3 for O, LSE, dQ, dK and dV; in addition the relative
 Frobenius error of each tensor must be <= 1e-2, which catches errors that the absolute
 bounds would let through when the tensor itself is small (O at N = 8192 has a standard
-deviation of about 0.018).
+deviation of about 0.018). The relative check is skipped when the reference's RMS is
+below 1e-4 (an exactly-zero gradient, e.g. dQ with a single visible key).
+
+Tests at softmax scales other than 1/sqrt(d) (not one of the five workloads) can produce
+gradients of magnitude 10 or more, where rounding the output to bf16 alone costs up to
+half an ulp = 2^-9 |x|; they pass rtol = 2^-7 (two half-ulps), applied elementwise on top
+of the absolute bound.
 """
 import numpy as np
 
@@ -47,15 +53,20 @@ def err_stats(got, ref):
             "rel_fro": float(fro) if d.size else 0.0}
 
 
-def assert_close(name, got, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS, rel_fro=REL_FRO):
+def assert_close(name, got, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS, rel_fro=REL_FRO,
+                 rtol=0.0):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     s = err_stats(got, ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    excess = float(np.max(np.abs(got - ref) - rtol * np.abs(ref))) if ref.size else 0.0
     print(f"  {name}: max_abs={s['max_abs']:.3e} mean_abs={s['mean_abs']:.3e} "
-          f"rel_fro={s['rel_fro']:.3e}", flush=True)
-    assert s["max_abs"] <= max_abs, (name, s)
+          f"rel_fro={s['rel_fro']:.3e} ref_rms={rms:.3e} max|ref|="
+          f"{float(np.max(np.abs(ref))) if ref.size else 0:.3e}", flush=True)
+    assert excess <= max_abs, (name, s, excess)
     assert s["mean_abs"] <= mean_abs, (name, s)
-    assert s["rel_fro"] <= rel_fro, (name, s)
+    if rms >= 1e-4:
+        assert s["rel_fro"] <= rel_fro, (name, s)
     return s
