@@ -13,6 +13,13 @@ kernel against MI355X's dense bf16 MFMA peak, and the fp64 CPU oracle timed on a
 sample of the same workload (the CPU baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibration MIB ...   also runs one plain device-to-device
+                                                     copy of MIB MiB before the timed
+                                                     region (reference kernel for the HBM
+                                                     byte counters FETCH_SIZE/WRITE_SIZE)
+       python bench.py --rocprof-summary DB [DB2]   prints a per-kernel table from
+                                                     rocprofv3 result databases (kernel
+                                                     trace, and counters if collected)
 """
 import argparse
 import json
@@ -76,12 +83,60 @@ def cpu_baseline(wl, budget_s=15.0):
                       f"same algorithmic FLOP count as the GPU metric"}
 
 
+def rocprof_summary(paths):
+    """Per-kernel summary of rocprofv3 SQLite output: calls, average duration, and the
+    average per-dispatch value of every collected counter."""
+    import glob
+    import sqlite3
+    for path in paths:
+        dbs = (glob.glob(os.path.join(path, "**", "*.db"), recursive=True)
+               if os.path.isdir(path) else glob.glob(path))
+        for db in sorted(dbs):
+            c = sqlite3.connect(db)
+            tabs = {r[0] for r in c.execute("select name from sqlite_master")}
+            print(f"# {os.path.basename(db)}")
+            if "kernels" in tabs and c.execute("select count(*) from kernels").fetchone()[0]:
+                rows = c.execute("select name, count(*), avg(duration), sum(duration) from "
+                                 "kernels group by name order by sum(duration) desc").fetchall()
+                tot = sum(r[3] for r in rows) or 1
+                print(f"{'calls':>5} {'avg_us':>10} {'pct':>6}  kernel")
+                for name, n, avg, sm in rows:
+                    print(f"{n:>5} {avg / 1e3:>10.2f} {100 * sm / tot:>6.2f}  {name[:110]}")
+            if "counters_collection" in tabs or "pmc_events" in tabs:
+                try:
+                    q = ("select kernel_name, counter_name, avg(value), count(*) from "
+                         "counters_collection group by kernel_name, counter_name "
+                         "order by kernel_name, counter_name")
+                    rows = c.execute(q).fetchall()
+                except sqlite3.Error:
+                    rows = []
+                for name, cn, val, n in rows:
+                    print(f"  {cn:<32} {val:>16.1f} per dispatch ({n} samples)  {name[:80]}")
+
+
+def copy_calibration(mib):
+    """One plain device copy of `mib` MiB (reads and writes that many bytes)."""
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def main():
+    if "--rocprof-summary" in sys.argv:
+        rocprof_summary(sys.argv[sys.argv.index("--rocprof-summary") + 1:])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -93,6 +148,8 @@ def main():
     import exact_io_aware_10_amd as fa
     from exact_io_aware_10_amd import inputs
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
     wl = WORKLOAD
     B, N, H, d, dtype, causal = wl["B"], wl["N"], wl["H"], wl["d"], wl["dtype"], wl["causal"]
     dev = torch.device("cuda:0")

@@ -1,5 +1,6 @@
 // C-ABI entry points of libfa_mi355x.so: synchronous argument checks, then kernel
 // launches on the caller's stream. Declarations and contracts: include/fa.h.
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -14,6 +15,12 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // (N + 256) * H * d limit: byte offsets of every row a kernel touches, including the
 // padded rows of a ragged last tile, fit in 31 bits.
 constexpr long kMaxSliceElems = 1L << 30;
+
+// Exponent scale |softmax_scale| * log2(e), kept >= the smallest normal float so that it
+// is strictly positive: masked scores (-inf) then give exp2(-inf) = 0 with no select, and
+// a zero softmax_scale still gives uniform weights (exp2 of products below 2^-100 is
+// exactly 1.0 in fp32).
+float exp_scale(float softmax_scale) { return fmaxf(fabsf(softmax_scale) * kLog2e, FLT_MIN); }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -68,7 +75,7 @@ FA_EXPORT fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
   a.N = N;
   a.H = H;
   a.T = B * N;
-  a.scale_log2 = fabsf(softmax_scale) * kLog2e;
+  a.scale_log2 = exp_scale(softmax_scale);
   a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
   return to_status(fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, false, stream));
 }
@@ -105,7 +112,7 @@ FA_EXPORT fa_status fa_bwd(const void* q, const void* k, const void* v, const vo
   a.H = H;
   a.T = B * N;
   a.scale = softmax_scale;
-  a.scale_log2 = fabsf(softmax_scale) * kLog2e;
+  a.scale_log2 = exp_scale(softmax_scale);
   a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
   return to_status(fa::launch_bwd(a, d, dtype == FA_BF16, causal != 0, false, stream));
 }
@@ -133,7 +140,7 @@ FA_EXPORT fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, v
   a.N = max_seqlen;
   a.H = H;
   a.T = total_tokens;
-  a.scale_log2 = fabsf(softmax_scale) * kLog2e;
+  a.scale_log2 = exp_scale(softmax_scale);
   a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
   return to_status(fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, true, stream));
 }

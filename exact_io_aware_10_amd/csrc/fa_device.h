@@ -53,6 +53,20 @@ __device__ __forceinline__ uint32_t pack2<F16>(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
+// acc + lo + hi of a packed 16-bit pair (v_dot2c_f32_{bf16,f16} against (1, 1)).
+template <class T>
+__device__ __forceinline__ float add_pair(uint32_t pair, float acc);
+template <>
+__device__ __forceinline__ float add_pair<BF16>(uint32_t pair, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
+template <>
+__device__ __forceinline__ float add_pair<F16>(uint32_t pair, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+}
+
 // 16-bit element -> fp32 (exact).
 template <class T>
 __device__ __forceinline__ float to_f32(uint32_t bits16);

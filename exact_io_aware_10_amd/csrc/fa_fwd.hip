@@ -8,17 +8,22 @@
 // inside the kernel ("FlashAttention 与算子融合", fusion table).
 //
 // Mapping onto CDNA4:
-//  - one workgroup = 4 waves = 128*CG query rows of one (batch or sequence, head); wave w
-//    owns 32*CG consecutive rows, held as MFMA B operands in registers for the whole loop.
-//  - key/value tiles of 64 rows are copied HBM/L2 -> registers -> LDS, double buffered:
-//    the loads for tile t+1 are issued before tile t is computed.
+//  - one workgroup = 4 waves = 128 query rows of one (batch or sequence, head); wave w
+//    owns 32 consecutive rows, held as MFMA B operands in registers for the whole loop.
+//  - key/value tiles of 64 rows go from HBM/L2 straight into LDS (buffer_load ... lds,
+//    bounds-checked so rows past the sequence read as zero), double buffered: the loads
+//    of tile t+1 are issued before tile t is computed. Rows are stored unpadded with an
+//    XOR swizzle of their 16-byte chunks that keeps the operand reads conflict-free.
 //  - scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: each lane then
 //    holds 32 scores of ONE query row (the other 32 sit in lane l^32), so row max and row
 //    sum need only per-lane work plus one v_permlane32_swap.
 //  - P^T leaves the accumulators already in the B-operand layout of the next MFMA,
-//    O^T += V^T P^T. V is written to LDS transposed, with key bits 2 and 3 swapped inside
-//    each group of 16, so that the key order of each lane's P registers matches the key
-//    order of a single 16-byte LDS read of V^T.
+//    O^T += V^T P^T. The V^T operand is read from the row-major V tile with
+//    ds_read_b64_tr_b16: in each group of 16 lanes, lane i names 4 consecutive values
+//    (row i of a 16x4 block) and lane j receives column j%4 of rows j/4, j/4+4, j/4+8,
+//    j/4+12. Lane i addresses key k0 + i/4, dims d0 + 4(i%4), so lane j receives dim
+//    d0 + j of keys k0..k0+3; two such reads give the 8 keys of one MFMA operand, in the
+//    key order of the P^T registers.
 //  - exp2 domain: scores are multiplied by scale*log2(e) in the exponent's FMA. The
 //    running max used as the exponent's reference is only moved when the true row max
 //    exceeds it by more than 8 (in log2 units), so the rescale of the output accumulator is
@@ -29,6 +34,10 @@
 namespace fa {
 namespace {
 
+#ifndef FA_FWD_OCC
+#define FA_FWD_OCC 2  // workgroups per CU the register budget is sized for
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBK = 64;                   // keys per tile
@@ -36,25 +45,35 @@ constexpr float kRescaleSlack = 8.0f;     // log2 units the reference max may la
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_inff();
 
-// Position of key k (0..63) inside a transposed V tile row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vpos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, class T, bool CAUSAL, bool VARLEN, int CG>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
-  constexpr int BQ = 32 * CG * kWaves;
-  constexpr int KSTR = D + 8;    // LDS row stride of K (elements): +16 B against bank conflicts
-  constexpr int VSTR = kBK + 8;  // LDS row stride of V^T (elements)
-  constexpr int DC = D / 16;     // 16-wide d chunks of Q K^T
-  constexpr int DB = D / 32;     // 32-wide d blocks of the output
-  constexpr int KC = kBK * D / 8 / kThreads;  // 16-byte K chunks per thread
-  constexpr int R = D / 32;                    // V rows per thread (transposed store)
-  constexpr int VKG = kBK / R;                 // V key groups
+// 16-byte-chunk swizzles of a tile row r (D/8 chunks per row).
+// K rows are read as 32 rows x one chunk (ds_read_b128): chunk c of row r sits at c ^ (r % D/8).
+// V rows are read 4 rows x 4 chunks per 32 lanes (ds_read_b64_tr_b16).
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBK * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
+template <int D, class T, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
+  constexpr int BQ = 32 * kWaves;
+  constexpr int ROWB = D * 2;                 // bytes per K/V row in LDS
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int TILEB = kBK * ROWB;           // bytes per tile
+  constexpr int RPL = 1024 / ROWB;            // rows per 1 KiB direct load (one per wave)
+  constexpr int LPW = TILEB / 1024 / kWaves;  // direct loads per wave per tile
+  constexpr int DC = D / 16;                  // 16-wide d chunks of Q K^T
+  constexpr int DB = D / 32;                  // 32-wide d blocks of the output
+
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks[2][TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs[2][TILEB];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- work item: (query block, head, batch or sequence)
   const int nqb = (a.N + BQ - 1) / BQ;
@@ -89,192 +108,161 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const auto ro = make_rsrc(a.o + base, nbytes);
   float* lse = a.lse + (VARLEN ? (long)h * a.T + tok0 : ((long)bs * a.H + h) * a.N);
 
-  const int wq0 = q0 + wave * 32 * CG;  // first query row of this wave
+  const int wq0 = q0 + wave * 32;  // first query row of this wave
+  const int qi = wq0 + l32;        // this lane's query row
   const int kend = CAUSAL ? (L < q0 + BQ ? L : q0 + BQ) : L;
   const int ntiles = (kend + kBK - 1) / kBK;
 
-  // ---- Q block into registers (B operand of S^T = K Q^T): lane holds row l32 of each
-  // 32-row group, d = 16*dc + 8g .. +7.
-  u32x4 qreg[CG][DC];
+  // ---- Q rows into registers (B operand of S^T = K Q^T): d = 16*dc + 8g .. +7
+  u32x4 qreg[DC];
 #pragma unroll
-  for (int cg = 0; cg < CG; ++cg)
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      u32x4 x = buf_load16(rq, (uint32_t)(wq0 + cg * 32 + l32) * rstride + (16 * dc + 8 * g) * 2);
-      qreg[cg][dc] = x ^ a.qsign;
-    }
+  for (int dc = 0; dc < DC; ++dc)
+    qreg[dc] = buf_load16(rq, (uint32_t)qi * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
 
-  // ---- tile loaders
-  u32x4 kr[KC], vr[R];
-  const int vkg = tid % VKG, vc = tid / VKG;  // V: keys R*vkg.., dims 8*vc..
-  auto gload = [&](int t) {
-    const int kb0 = t * kBK;
+  // ---- direct HBM/L2 -> LDS tile loads: this wave fills LPW 1 KiB blocks of each tile;
+  // lane l of a block writes row blk*RPL + l/CPR, physical chunk l%CPR.
+  const int lrow = lane / CPR, lpc = lane % CPR;
+  auto tload = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* tile, int t, bool is_k) {
 #pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = tid + kThreads * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
-      kr[i] = buf_load16(rk, (uint32_t)(kb0 + row) * rstride + col * 2);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      vr[r] = buf_load16(rv, (uint32_t)(kb0 + R * vkg + r) * rstride + vc * 16);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = tid + kThreads * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KSTR + col]) = kr[i];
-    }
-    const int p = vpos(R * vkg);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // dims 8*vc + 2e (low halves) and 8*vc + 2e + 1 (high halves)
-      if constexpr (R == 4) {
-        u32x2 lo = {__builtin_amdgcn_perm(vr[1][e], vr[0][e], 0x05040100u),
-                    __builtin_amdgcn_perm(vr[3][e], vr[2][e], 0x05040100u)};
-        u32x2 hi = {__builtin_amdgcn_perm(vr[1][e], vr[0][e], 0x07060302u),
-                    __builtin_amdgcn_perm(vr[3][e], vr[2][e], 0x07060302u)};
-        *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * e) * VSTR + p]) = lo;
-        *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * e + 1) * VSTR + p]) = hi;
-      } else {
-        *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * vc + 2 * e) * VSTR + p]) =
-            __builtin_amdgcn_perm(vr[1][e], vr[0][e], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * vc + 2 * e + 1) * VSTR + p]) =
-            __builtin_amdgcn_perm(vr[1][e], vr[0][e], 0x07060302u);
-      }
+    for (int j = 0; j < LPW; ++j) {
+      const int blk = wave * LPW + j;
+      const int row = blk * RPL + lrow;
+      const int c = lpc ^ (is_k ? kswz<D>(row) : vswz<D>(row));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void*)(tile + blk * 1024), 16,
+          (uint32_t)(t * kBK + row) * rstride + c * 16, 0, 0, 0);
     }
   };
 
-  // ---- running state per 32-row group: reference max (log2 units), partial row sum
-  // over this lane's keys, unnormalised output O^T (lane = row, registers = d).
-  float mref[CG], lsum[CG];
-  f32x16 oacc[CG][DB];
+  // ---- per-lane LDS byte offsets of the MFMA operand reads
+  // K (A operand of S^T): row kb*32 + l32, logical chunk 2*dc + g
+  const int krow_off = l32 * ROWB;
+  // V^T (A operand of O^T): tr reads of keys kc*16 + 4g + i/4 (+8), dims db*32 + 16G + 4(i%4)
+  const int i16 = lane & 15, G = (lane >> 4) & 1;
+  const int vkey = 4 * g + (i16 >> 2);
+  const int vsw = vswz<D>(vkey);
+  const int vhalf = 8 * (i16 & 1);
+
+  float mref = kNegInf, lsum = 0.f;
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int cg = 0; cg < CG; ++cg) {
-    mref[cg] = kNegInf;
-    lsum[cg] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[cg][db] = f32x16{};
-  }
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   const float c2 = a.scale_log2;
 
-  gload(0);
-  lstore(0);
+  tload(rk, Ks[0], 0, true);
+  tload(rv, Vs[0], 0, false);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+    if (t + 1 < ntiles) {
+      tload(rk, Ks[buf ^ 1], t + 1, true);
+      tload(rv, Vs[buf ^ 1], t + 1, false);
+    }
     const int kt0 = t * kBK;
-    const bool active = !CAUSAL || kt0 <= wq0 + 32 * CG - 1;
+    const bool active = !CAUSAL || kt0 <= wq0 + 31;
     if (active) {
-      // S^T tile: two 32-key blocks x CG 32-query groups
-      f32x16 s[CG][2];
-#pragma unroll
-      for (int cg = 0; cg < CG; ++cg) s[cg][0] = s[cg][1] = f32x16{};
+      // S^T tile: two 32-key blocks
+      f32x16 s[2];
+      s[0] = s[1] = f32x16{};
+      const uint8_t* kt = Ks[buf];
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+          const int c = (2 * dc + g) ^ kswz<D>(l32);  // row kb*32 + l32 has the same swizzle
           const u32x4 ka =
-              *reinterpret_cast<const u32x4*>(&Ks[buf][(kb * 32 + l32) * KSTR + 16 * dc + 8 * g]);
-#pragma unroll
-          for (int cg = 0; cg < CG; ++cg) s[cg][kb] = mfma32<T>(ka, qreg[cg][dc], s[cg][kb]);
+              *reinterpret_cast<const u32x4*>(kt + kb * 32 * ROWB + krow_off + c * 16);
+          s[kb] = mfma32<T>(ka, qreg[dc], s[kb]);
         }
 
       const bool masked = kt0 + kBK > L || (CAUSAL && kt0 + kBK - 1 > wq0);
-      u32x4 pf[CG][4];
-#pragma unroll
-      for (int cg = 0; cg < CG; ++cg) {
-        const int qi = wq0 + cg * 32 + l32;
-        if (masked) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-              if (key >= L || (CAUSAL && key > qi)) s[cg][kb][r] = kNegInf;
-            }
-        }
-        float mx = s[cg][0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cg][kb][r]);
-        mx = pair_max(mx);
-        const float mnew = mx == kNegInf ? kNegInf : mx * c2;
-        const bool need = mnew > mref[cg] + kRescaleSlack;
-        if (__any(need)) {
-          const float alpha = need ? exp2f_hw(mref[cg] - mnew) : 1.0f;
-          lsum[cg] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[cg][db] *= alpha;
-          if (need) mref[cg] = mnew;
-        }
-        const float mu = mref[cg] == kNegInf ? 0.f : mref[cg];
-        float p[32];
+      if (masked) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float sv = s[cg][kb][r];
-            float e = exp2f_hw(fmaf(sv, c2, -mu));
-            if (masked) e = sv == kNegInf ? 0.f : e;
-            p[kb * 16 + r] = e;
+            const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= L || (CAUSAL && key > qi)) s[kb][r] = kNegInf;
           }
-        float ls = 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) ls += p[i];
-        lsum[cg] += ls;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          pf[cg][kc] = u32x4{pack2<T>(p[8 * kc + 0], p[8 * kc + 1]),
-                             pack2<T>(p[8 * kc + 2], p[8 * kc + 3]),
-                             pack2<T>(p[8 * kc + 4], p[8 * kc + 5]),
-                             pack2<T>(p[8 * kc + 6], p[8 * kc + 7])};
       }
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      const float mnew = pair_max(mx) * c2;  // c2 > 0: a fully masked row keeps -inf
+      const bool need = mnew > mref + kRescaleSlack;
+      if (__any(need)) {
+        const float alpha = need ? exp2f_hw(mref - mnew) : 1.0f;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        if (need) mref = mnew;
+      }
+      // masked scores are -inf and c2 > 0, so their exponent is exactly 0
+      const float mu = mref == kNegInf ? 0.f : mref;
+      u32x4 pf[4];
+      float ls = lsum;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = 8 * kc + j;
+          p[j] = exp2f_hw(fmaf(s[r >> 4][r & 15], c2, -mu));
+        }
+        // P rounded to the element type; the row sum adds exactly the rounded values
+        pf[kc] = u32x4{pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]),
+                       pack2<T>(p[6], p[7])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ls = add_pair<T>(pf[kc][e], ls);
+      }
+      lsum = ls;
 
       // O^T += V^T P^T over four 16-key chunks
+      const uint8_t* vt = Vs[buf];
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 va =
-              *reinterpret_cast<const u32x4*>(&Vt[buf][(db * 32 + l32) * VSTR + 16 * kc + 8 * g]);
-#pragma unroll
-          for (int cg = 0; cg < CG; ++cg) oacc[cg][db] = mfma32<T>(va, pf[cg][kc], oacc[cg][db]);
+          const int c = (db * 4 + 2 * G + ((i16 & 3) >> 1)) ^ vsw;
+          const int off = (kc * 16 + vkey) * ROWB + c * 16 + vhalf;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + off));
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + off + 8 * ROWB));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 va = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          oacc[db] = mfma32<T>(va, pf[kc], oacc[db]);
         }
     }
-    if (t + 1 < ntiles) lstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's tile t+1 loads have landed in LDS
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / l (rows >= L are dropped by the buffer bounds), LSE
+  const float l = pair_sum(lsum);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-  for (int cg = 0; cg < CG; ++cg) {
-    const int qi = wq0 + cg * 32 + l32;
-    const float l = pair_sum(lsum[cg]);
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f32x16& o = oacc[cg][db];
-        u32x2 v = {pack2<T>(o[4 * rr] * inv, o[4 * rr + 1] * inv),
-                   pack2<T>(o[4 * rr + 2] * inv, o[4 * rr + 3] * inv)};
-        buf_store8(ro, (uint32_t)qi * rstride + (db * 32 + 8 * rr + 4 * g) * 2, v);
-      }
-    if (g == 0 && qi < L) lse[qi] = l > 0.f ? (mref[cg] + log2f_hw(l)) * kLn2 : kNegInf;
-  }
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x16& o = oacc[db];
+      u32x2 v = {pack2<T>(o[4 * rr] * inv, o[4 * rr + 1] * inv),
+                 pack2<T>(o[4 * rr + 2] * inv, o[4 * rr + 3] * inv)};
+      buf_store8(ro, (uint32_t)qi * rstride + (db * 32 + 8 * rr + 4 * g) * 2, v);
+    }
+  if (g == 0 && qi < L) lse[qi] = l > 0.f ? (mref + log2f_hw(l)) * kLn2 : kNegInf;
 }
 
 template <int D, class T, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdArgs& a, hipStream_t st) {
-  constexpr int CG = 1;
-  constexpr int BQ = 32 * CG * kWaves;
+  constexpr int BQ = 32 * kWaves;
   const int nqb = (a.N + BQ - 1) / BQ;
   const long total = (long)nqb * a.H * a.B;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, VARLEN, CG>), dim3((unsigned)total),
+  hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)total),
                      dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
