@@ -28,6 +28,8 @@
 //    running max used as the exponent's reference is only moved when the true row max
 //    exceeds it by more than 8 (in log2 units), so the rescale of the output accumulator is
 //    rare; O = acc / l and LSE = (m_ref + log2 l) ln 2 are exact for any reference.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -68,8 +70,12 @@ __global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
   constexpr int DC = D / 16;                  // 16-wide d chunks of Q K^T
   constexpr int DB = D / 32;                  // 32-wide d blocks of the output
 
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks[2][TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs[2][TILEB];
+  // separate objects per buffer: the compiler can then see that the direct loads into one
+  // buffer do not alias the reads of the other and need not wait for them
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs1[TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
@@ -149,16 +155,16 @@ __global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   const float c2 = a.scale_log2;
 
-  tload(rk, Ks[0], 0, true);
-  tload(rv, Vs[0], 0, false);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  // one pipeline step on tile t held in buffer B (B = t % 2): issue the direct loads of
+  // tile t+1 into the other buffer, compute tile t, then wait for this wave's loads and
+  // meet the other waves at the barrier.
+  auto step = [&](auto bsel, int t) {
+    constexpr int B = decltype(bsel)::value;
+    const uint8_t* kt = B ? Ks1 : Ks0;
+    const uint8_t* vt = B ? Vs1 : Vs0;
     if (t + 1 < ntiles) {
-      tload(rk, Ks[buf ^ 1], t + 1, true);
-      tload(rv, Vs[buf ^ 1], t + 1, false);
+      tload(rk, B ? Ks0 : Ks1, t + 1, true);
+      tload(rv, B ? Vs0 : Vs1, t + 1, false);
     }
     const int kt0 = t * kBK;
     const bool active = !CAUSAL || kt0 <= wq0 + 31;
@@ -166,7 +172,6 @@ __global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
       // S^T tile: two 32-key blocks
       f32x16 s[2];
       s[0] = s[1] = f32x16{};
-      const uint8_t* kt = Ks[buf];
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
@@ -179,6 +184,8 @@ __global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
 
       const bool masked = kt0 + kBK > L || (CAUSAL && kt0 + kBK - 1 > wq0);
       if (masked) {
+        // a real branch: keeps the per-element mask out of the unmasked tiles
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -222,7 +229,6 @@ __global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
       lsum = ls;
 
       // O^T += V^T P^T over four 16-key chunks
-      const uint8_t* vt = Vs[buf];
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
@@ -239,6 +245,15 @@ __global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's tile t+1 loads have landed in LDS
     __syncthreads();
+  };
+
+  tload(rk, Ks0, 0, true);
+  tload(rv, Vs0, 0, false);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   // ---- epilogue: O = acc / l (rows >= L are dropped by the buffer bounds), LSE
