@@ -82,7 +82,7 @@ FA_EXPORT fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
 
 FA_EXPORT size_t fa_bwd_workspace_size(int B, int N, int H, int d) {
   if (B < 0 || N < 0 || H < 0 || (d != 64 && d != 128)) return 0;
-  return (size_t)4 * B * H * N;
+  return (size_t)8 * B * H * N;
 }
 
 FA_EXPORT fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -105,7 +105,8 @@ FA_EXPORT fa_status fa_bwd(const void* q, const void* k, const void* v, const vo
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  a.delta = static_cast<float*>(workspace);
+  a.neg_delta = static_cast<float*>(workspace);
+  a.neg_lse2 = a.neg_delta + (long)B * H * N;
   a.cu = nullptr;
   a.B = B;
   a.N = N;

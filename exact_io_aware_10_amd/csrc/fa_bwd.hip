@@ -11,19 +11,25 @@
 //   dQ_i = scale sum_j dS_ij k_j,                  dK_j = scale sum_i dS_ij q_i
 //
 // Three launches, no floating-point atomics (bitwise deterministic):
-//   1. bwd_delta_kernel : D_i for every row (reads O and dO once).
-//   2. bwd_dkdv_kernel  : one workgroup per 128-key block (32 keys per wave, K and V held
-//                         in registers); streams 64-query tiles of Q and dO through LDS,
-//                         double buffered, each stored row-major and transposed.
-//                         S = Q K^T and dP = dO V^T are computed with lanes <-> keys, so
-//                         P and dS leave the accumulators in the B-operand layout of
-//                         dV^T += dO^T P and dK^T += Q^T dS.
-//   3. bwd_dq_kernel    : one workgroup per 128-query block (32 queries per wave, Q and
-//                         dO in registers); streams 64-key tiles of K and V; S^T and dP^T
-//                         with lanes <-> queries feed dQ^T += K^T dS^T.
-// The transposed LDS copies use the same key/query bit permutation as the forward kernel
-// (bits 2 and 3 swapped within groups of 16) so one 16-byte LDS read matches the row order
-// of the P / dS registers.
+//   1. bwd_prep_kernel : per row, -D_i and -LSE_i log2(e) into the workspace.
+//   2. bwd_dkdv_kernel : one workgroup per 128-key block (32 keys per wave; K and V held
+//                        in registers); streams 64-query tiles of Q, dO and the two row
+//                        terms from HBM/L2 straight into LDS, double buffered.
+//                        S = Q K^T and dP = dO V^T are computed with lanes <-> keys, so P
+//                        and dS leave the accumulators in the B-operand layout of
+//                        dV^T += dO^T P and dK^T += Q^T dS.
+//   3. bwd_dq_kernel   : one workgroup per 128-query block (32 queries per wave; Q and dO
+//                        in registers); streams 64-key tiles of K and V; S^T and dP^T with
+//                        lanes <-> queries feed dQ^T += K^T dS^T.
+// Each streamed tile is stored once, row-major, and read both as row fragments
+// (ds_read_b128: operand rows = tile rows) and as transposed fragments
+// (ds_read_b64_tr_b16: operand rows = tile columns; in each group of 16 lanes, lane i names
+// 4 consecutive values and lane j receives column j%4 of rows j/4 + 4k, k = 0..3). The
+// 16-byte chunks of row r are XOR-swizzled by f(r) = ((r&3)<<2)|((r>>2)&3) (d = 128), which
+// makes both read patterns conflict-free.
+// -D is loaded as the initial value of the dP accumulators, so dS = P * acc.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -34,15 +40,23 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;  // rows of the streamed tile (queries in dK/dV, keys in dQ)
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kInf = __builtin_inff();
 
-__device__ __forceinline__ int tpos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Per-slice addressing shared by the three kernels.
+// Chunk swizzle of tile row r, good for both row and transposed fragment reads.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Per-slice addressing shared by the kernels.
 struct SliceInfo {
   long tok0;  // first token of the slice in the [tokens, H, d] tensors
   int L;      // rows in the slice
-  long stat;  // offset of row 0 of the slice in lse / delta
+  long stat;  // offset of row 0 of the slice in lse / the workspace row terms
 };
 
 __device__ __forceinline__ SliceInfo slice_info(const BwdArgs& a, int bs, int h) {
@@ -62,9 +76,20 @@ __device__ __forceinline__ SliceInfo slice_info(const BwdArgs& a, int bs, int h)
   return s;
 }
 
-// ---------------------------------------------------------------- 1. D_i = <dO_i, O_i>
+// Work item of a dense or packed launch: (block index within the slice, head, batch/seq).
+__device__ __forceinline__ void decode_work(const BwdArgs& a, int nblk, bool varlen, int& blk,
+                                            int& h, int& bs) {
+  uint32_t w = blockIdx.x;
+  if (!varlen) w = xcd_remap(w, gridDim.x);
+  blk = w % nblk;
+  h = (w / nblk) % a.H;
+  bs = w / (nblk * a.H);
+}
+
+// ---------------------------------------------------------------- 1. row terms
+// ws[0 .. rows) = -D_i = -<dO_i, O_i>;  ws[rows .. 2 rows) = -LSE_i * log2(e)
 template <int D, class T>
-__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdArgs a, long rows) {
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a, long rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   const long row = (long)blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
   const int c = threadIdx.x % TPR;
@@ -92,82 +117,74 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdArgs a, long row
     } else {
       idx = (long)h * a.T + tok;
     }
-    a.delta[idx] = acc;
+    a.neg_delta[idx] = -acc;
+    a.neg_lse2[idx] = -a.lse[idx] * kLog2e;
   }
 }
 
-// ---------------------------------------------------------------- shared tile loader
-// A tile of kTile rows x D of a [tokens, H, D] tensor, loaded so that each thread holds R
-// consecutive rows x 8 columns; stored to LDS row-major (stride D+8) and/or transposed
-// (stride kTile+8, rows permuted by tpos).
+// ---------------------------------------------------------------- tile access helpers
 template <int D>
-struct TileLoader {
-  static constexpr int R = kTile * D / 8 / kThreads;  // rows per thread (4 or 2)
-  static constexpr int KG = kTile / R;
-  static constexpr int RSTR = D + 8;
-  static constexpr int TSTR = kTile + 8;
-  int kg, c;
-  u32x4 r[R];
-  __device__ TileLoader(int tid) : kg(tid % KG), c(tid / KG) {}
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t rstride, int row0,
-                                       uint32_t flip) {
+struct Tile {
+  static constexpr int ROWB = D * 2;        // bytes per row
+  static constexpr int CPR = D / 8;         // 16-byte chunks per row
+  static constexpr int BYTES = kTile * ROWB;
+  static constexpr int RPL = 1024 / ROWB;   // rows per 1 KiB direct load
+  static constexpr int LPW = BYTES / 1024 / kWaves;  // direct loads per wave per tile
+
+  // direct HBM/L2 -> LDS load of tile rows [row0, row0 + kTile) of a [tokens, H, D] tensor
+  static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint8_t* tile,
+                                              int row0, uint32_t rstride, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-      r[i] = buf_load16(rs, (uint32_t)(row0 + R * kg + i) * rstride + c * 16) ^ flip;
-  }
-  __device__ __forceinline__ void store_rows(uint16_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-      *reinterpret_cast<u32x4*>(&lds[(R * kg + i) * RSTR + 8 * c]) = r[i];
-  }
-  __device__ __forceinline__ void store_transposed(uint16_t* lds) const {
-    const int p = tpos(R * kg);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (R == 4) {
-        u32x2 lo = {__builtin_amdgcn_perm(r[1][e], r[0][e], 0x05040100u),
-                    __builtin_amdgcn_perm(r[3][e], r[2][e], 0x05040100u)};
-        u32x2 hi = {__builtin_amdgcn_perm(r[1][e], r[0][e], 0x07060302u),
-                    __builtin_amdgcn_perm(r[3][e], r[2][e], 0x07060302u)};
-        *reinterpret_cast<u32x2*>(&lds[(8 * c + 2 * e) * TSTR + p]) = lo;
-        *reinterpret_cast<u32x2*>(&lds[(8 * c + 2 * e + 1) * TSTR + p]) = hi;
-      } else {
-        *reinterpret_cast<uint32_t*>(&lds[(8 * c + 2 * e) * TSTR + p]) =
-            __builtin_amdgcn_perm(r[1][e], r[0][e], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(&lds[(8 * c + 2 * e + 1) * TSTR + p]) =
-            __builtin_amdgcn_perm(r[1][e], r[0][e], 0x07060302u);
-      }
+    for (int j = 0; j < LPW; ++j) {
+      const int blk = wave * LPW + j;
+      const int row = blk * RPL + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(row);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + blk * 1024), 16,
+                                               (uint32_t)(row0 + row) * rstride + c * 16, 0,
+                                               0, 0);
     }
   }
+  // row fragment: row r, logical chunk c (16 bytes)
+  static __device__ __forceinline__ u32x4 row_frag(const uint8_t* tile, int r, int c) {
+    return *reinterpret_cast<const u32x4*>(tile + r * ROWB + ((c ^ swz<D>(r)) << 4));
+  }
+  // transposed fragment (A operand of a 32x32x16 MFMA over 16 tile rows k0..k0+15 and 32
+  // tile columns d0..d0+31): lane (l32, g) gets column d0 + l32 of rows
+  // k0 + 4g + {0,1,2,3} and k0 + 8 + 4g + {0,1,2,3}, matching the row order of P / dS
+  // registers taken from a 32x32 accumulator.
+  static __device__ __forceinline__ u32x4 tr_frag(const uint8_t* tile, int k0, int d0, int lane) {
+    const int i16 = lane & 15, G = (lane >> 4) & 1, g = lane >> 5;
+    const int r = k0 + 4 * g + (i16 >> 2);
+    const int c = (d0 >> 3) + 2 * G + ((i16 & 3) >> 1);
+    const int half = 8 * (i16 & 1);
+    const uint8_t* p0 = tile + r * ROWB + ((c ^ swz<D>(r)) << 4) + half;
+    const uint8_t* p1 = tile + (r + 8) * ROWB + ((c ^ swz<D>(r + 8)) << 4) + half;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+  }
 };
-
-// Work item of a dense or packed launch: (block index within the slice, head, batch/seq).
-__device__ __forceinline__ void decode_work(const BwdArgs& a, int nblk, bool varlen, int& blk,
-                                            int& h, int& bs) {
-  uint32_t w = blockIdx.x;
-  if (!varlen) w = xcd_remap(w, gridDim.x);
-  blk = w % nblk;
-  h = (w / nblk) % a.H;
-  bs = w / (nblk * a.H);
-}
 
 // ---------------------------------------------------------------- 2. dK, dV
 template <int D, class T, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BKV = 32 * kWaves;  // keys per workgroup
   constexpr int DC = D / 16, DB = D / 32;
-  using TL = TileLoader<D>;
-  constexpr int RSTR = TL::RSTR, TSTR = TL::TSTR;
+  using TL = Tile<D>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][kTile * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][kTile * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[2][D * TSTR];
-  __shared__ __attribute__((aligned(16))) float lse2s[2][kTile];
-  __shared__ __attribute__((aligned(16))) float dds[2][kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t Qs0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Qs1[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dOs0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dOs1[TL::BYTES];
+  __shared__ __attribute__((aligned(256))) float nl0[kTile];  // -LSE log2(e)
+  __shared__ __attribute__((aligned(256))) float nl1[kTile];
+  __shared__ __attribute__((aligned(256))) float nd0[kTile];  // -D
+  __shared__ __attribute__((aligned(256))) float nd1[kTile];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nkb = (a.N + BKV - 1) / BKV;
   int kb, h, bs;
   decode_work(a, nkb, VARLEN, kb, h, bs);
@@ -185,17 +202,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const auto rdo = make_rsrc(a.dout + base, nbytes);
   const auto rdk = make_rsrc(a.dk + base, nbytes);
   const auto rdv = make_rsrc(a.dv + base, nbytes);
-  const float* lse = a.lse + si.stat;
-  const float* delta = a.delta + si.stat;
+  const auto rnl = make_rsrc(a.neg_lse2 + si.stat, (uint32_t)L * 4);
+  const auto rnd = make_rsrc(a.neg_delta + si.stat, (uint32_t)L * 4);
 
   const int wk0 = k0 + wave * 32;  // this wave's keys: wk0 .. wk0+31
   const int key = wk0 + l32;       // the key this lane's accumulators belong to
 
-  // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T
+  // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T. A negative
+  // softmax scale is folded into K's sign (the gradient below then uses the signed scale).
   u32x4 kreg[DC], vreg[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) {
-    kreg[dc] = buf_load16(rk, (uint32_t)key * rstride + (16 * dc + 8 * g) * 2);
+    kreg[dc] = buf_load16(rk, (uint32_t)key * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
     vreg[dc] = buf_load16(rv, (uint32_t)key * rstride + (16 * dc + 8 * g) * 2);
   }
 
@@ -207,101 +225,93 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int qt_end = (L + kTile - 1) / kTile;
   const float c2 = a.scale_log2;
 
-  TL tq(tid), tdo(tid);
-  float lse2_next = 0.f, dd_next = 0.f;
-  auto gload = [&](int qt) {
-    const int r0 = qt * kTile;
-    tq.load(rq, rstride, r0, a.qsign);
-    tdo.load(rdo, rstride, r0, 0u);
-    if (tid < kTile) {
-      const int qi = r0 + tid;
-      lse2_next = qi < L ? lse[qi] * kLog2e : kInf;
-      dd_next = qi < L ? delta[qi] : 0.f;
-    }
-  };
-  auto lstore = [&](int buf) {
-    tq.store_rows(Qs[buf]);
-    tq.store_transposed(Qt[buf]);
-    tdo.store_rows(dOs[buf]);
-    tdo.store_transposed(dOt[buf]);
-    if (tid < kTile) {
-      lse2s[buf][tid] = lse2_next;
-      dds[buf][tid] = dd_next;
+  auto load_tile = [&](int qt, uint8_t* qs, uint8_t* dos, float* nl, float* nd) {
+    TL::load(rq, qs, qt * kTile, rstride, wave, lane);
+    TL::load(rdo, dos, qt * kTile, rstride, wave, lane);
+    if (wave == 0) {  // 64 lanes x 4 bytes: one row term per query of the tile
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rnl, (lds_void*)nl, 4, (qt * kTile + lane) * 4,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rnd, (lds_void*)nd, 4, (qt * kTile + lane) * 4,
+                                               0, 0, 0);
     }
   };
 
-  if (qt_begin < qt_end) {
-    gload(qt_begin);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int qt = qt_begin; qt < qt_end; ++qt) {
-    const int buf = (qt - qt_begin) & 1;
-    if (qt + 1 < qt_end) gload(qt + 1);
+  auto step = [&](auto bsel, int qt) {
+    constexpr int B = decltype(bsel)::value;
+    const uint8_t* qs = B ? Qs1 : Qs0;
+    const uint8_t* dos = B ? dOs1 : dOs0;
+    const float* nl = B ? nl1 : nl0;
+    const float* nd = B ? nd1 : nd0;
+    if (qt + 1 < qt_end) load_tile(qt + 1, B ? Qs0 : Qs1, B ? dOs0 : dOs1, B ? nl0 : nl1,
+                                   B ? nd0 : nd1);
     const int q0 = qt * kTile;
     const bool active = !CAUSAL || q0 + kTile - 1 >= wk0;
     if (active) {
-      f32x16 s[2], dp[2];
-      s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int off = (qb * 32 + l32) * RSTR + 16 * dc + 8 * g;
-          const u32x4 qa = *reinterpret_cast<const u32x4*>(&Qs[buf][off]);
-          const u32x4 da = *reinterpret_cast<const u32x4*>(&dOs[buf][off]);
-          s[qb] = mfma32<T>(qa, kreg[dc], s[qb]);
-          dp[qb] = mfma32<T>(da, vreg[dc], dp[qb]);
-        }
       const bool diag = CAUSAL && q0 < wk0 + 31;
-      u32x4 pf[4], sf[4];
+      // the two 32-query halves of the tile, one after the other
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        float p[16], ds[16];
+        // S (queries x keys) and dP - D (the accumulator starts at -D of each query)
+        f32x16 s = f32x16{}, dp;
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          const int ql = qb * 32 + 8 * a4 + 4 * g;  // local query of registers 4*a4 ..
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[buf][ql]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dds[buf][ql]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&nd[qb * 32 + 8 * a4 + 4 * g]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * a4 + j;
-            float e = exp2f_hw(fmaf(s[qb][r], c2, -l4[j]));
-            if (diag && key > q0 + ql + j) e = 0.f;
-            p[r] = e;
-            ds[r] = e * (dp[qb][r] - d4[j]);
-          }
+          for (int j = 0; j < 4; ++j) dp[4 * a4 + j] = d4[j];
+        }
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          s = mfma32<T>(TL::row_frag(qs, qb * 32 + l32, 2 * dc + g), kreg[dc], s);
+          dp = mfma32<T>(TL::row_frag(dos, qb * 32 + l32, 2 * dc + g), vreg[dc], dp);
+        }
+        float p[16];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&nl[qb * 32 + 8 * a4 + 4 * g]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[4 * a4 + j] = exp2f_hw(fmaf(s[4 * a4 + j], c2, l4[j]));
+        }
+        if (diag) {
+          __builtin_amdgcn_sched_barrier(0);  // keep the mask a branch (diagonal tiles only)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key > q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) p[r] = 0.f;
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          pf[2 * qb + hh] = u32x4{pack2<T>(p[8 * hh + 0], p[8 * hh + 1]),
-                                  pack2<T>(p[8 * hh + 2], p[8 * hh + 3]),
-                                  pack2<T>(p[8 * hh + 4], p[8 * hh + 5]),
-                                  pack2<T>(p[8 * hh + 6], p[8 * hh + 7])};
-          sf[2 * qb + hh] = u32x4{pack2<T>(ds[8 * hh + 0], ds[8 * hh + 1]),
-                                  pack2<T>(ds[8 * hh + 2], ds[8 * hh + 3]),
-                                  pack2<T>(ds[8 * hh + 4], ds[8 * hh + 5]),
-                                  pack2<T>(ds[8 * hh + 6], ds[8 * hh + 7])};
+          float ds[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ds[j] = p[8 * hh + j] * dp[8 * hh + j];
+          const u32x4 pf = {pack2<T>(p[8 * hh + 0], p[8 * hh + 1]),
+                            pack2<T>(p[8 * hh + 2], p[8 * hh + 3]),
+                            pack2<T>(p[8 * hh + 4], p[8 * hh + 5]),
+                            pack2<T>(p[8 * hh + 6], p[8 * hh + 7])};
+          const u32x4 sf = {pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]),
+                            pack2<T>(ds[4], ds[5]), pack2<T>(ds[6], ds[7])};
+          // dV^T += dO^T P and dK^T += Q^T dS over the 16-query chunk 2 qb + hh
+          const int kc = 2 * qb + hh;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dvacc[db] = mfma32<T>(TL::tr_frag(dos, kc * 16, db * 32, lane), pf, dvacc[db]);
+            dkacc[db] = mfma32<T>(TL::tr_frag(qs, kc * 16, db * 32, lane), sf, dkacc[db]);
+          }
         }
       }
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int off = (db * 32 + l32) * TSTR + 16 * kc + 8 * g;
-          const u32x4 doa = *reinterpret_cast<const u32x4*>(&dOt[buf][off]);
-          const u32x4 qa = *reinterpret_cast<const u32x4*>(&Qt[buf][off]);
-          dvacc[db] = mfma32<T>(doa, pf[kc], dvacc[db]);
-          dkacc[db] = mfma32<T>(qa, sf[kc], dkacc[db]);
-        }
     }
-    if (qt + 1 < qt_end) lstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
     __syncthreads();
+  };
+
+  load_tile(qt_begin, Qs0, dOs0, nl0, nd0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int qt = qt_begin; qt < qt_end; qt += 2) {
+    step(std::integral_constant<int, 0>{}, qt);
+    if (qt + 1 < qt_end) step(std::integral_constant<int, 1>{}, qt + 1);
   }
 
-  // dK = |scale| * sum dS q' (q' = q with the sign of scale folded in), dV = sum P dO
-  const float ks = fabsf(a.scale);
+  // dK = scale * sum dS q (signed scale), dV = sum P dO
+  const float ks = a.scale;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -321,15 +331,16 @@ template <int D, class T, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BQ = 32 * kWaves;
   constexpr int DC = D / 16, DB = D / 32;
-  using TL = TileLoader<D>;
-  constexpr int RSTR = TL::RSTR, TSTR = TL::TSTR;
+  using TL = Tile<D>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTile * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kTile * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TSTR];
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks1[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs1[TL::BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nqb = (a.N + BQ - 1) / BQ;
   int qb, h, bs;
   decode_work(a, nqb, VARLEN, qb, h, bs);
@@ -356,8 +367,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     qreg[dc] = buf_load16(rq, (uint32_t)qi * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
     doreg[dc] = buf_load16(rdo, (uint32_t)qi * rstride + (16 * dc + 8 * g) * 2);
   }
-  const float lse2 = qi < L ? a.lse[si.stat + qi] * kLog2e : kInf;
-  const float dd = qi < L ? a.delta[si.stat + qi] : 0.f;
+  const float nlq = qi < L ? a.neg_lse2[si.stat + qi] : 0.f;
+  const float ndq = qi < L ? a.neg_delta[si.stat + qi] : 0.f;
 
   f32x16 dqacc[DB];
 #pragma unroll
@@ -367,68 +378,72 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int ntiles = (kend + kTile - 1) / kTile;
   const float c2 = a.scale_log2;
 
-  TL tk(tid), tv(tid);
-  auto gload = [&](int t) {
-    tk.load(rk, rstride, t * kTile, 0u);
-    tv.load(rv, rstride, t * kTile, 0u);
-  };
-  auto lstore = [&](int buf) {
-    tk.store_rows(Ks[buf]);
-    tk.store_transposed(Kt[buf]);
-    tv.store_rows(Vs[buf]);
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+  auto step = [&](auto bsel, int t) {
+    constexpr int B = decltype(bsel)::value;
+    const uint8_t* ks = B ? Ks1 : Ks0;
+    const uint8_t* vs = B ? Vs1 : Vs0;
+    if (t + 1 < ntiles) {
+      TL::load(rk, B ? Ks0 : Ks1, (t + 1) * kTile, rstride, wave, lane);
+      TL::load(rv, B ? Vs0 : Vs1, (t + 1) * kTile, rstride, wave, lane);
+    }
     const int kt0 = t * kTile;
     const bool active = !CAUSAL || kt0 <= wq0 + 31;
     if (active) {
+      // S^T and dP^T - D (keys x queries), two 32-key blocks
       f32x16 s[2], dp[2];
-      s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[kb][r] = ndq;
+      }
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int off = (kb * 32 + l32) * RSTR + 16 * dc + 8 * g;
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(&Ks[buf][off]);
-          const u32x4 va = *reinterpret_cast<const u32x4*>(&Vs[buf][off]);
-          s[kb] = mfma32<T>(ka, qreg[dc], s[kb]);
-          dp[kb] = mfma32<T>(va, doreg[dc], dp[kb]);
+          s[kb] = mfma32<T>(TL::row_frag(ks, kb * 32 + l32, 2 * dc + g), qreg[dc], s[kb]);
+          dp[kb] = mfma32<T>(TL::row_frag(vs, kb * 32 + l32, 2 * dc + g), doreg[dc], dp[kb]);
         }
-      const bool masked = kt0 + kTile > L || (CAUSAL && kt0 + kTile - 1 > wq0);
-      float ds[32];
+      float p[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = exp2f_hw(fmaf(s[kb][r], c2, -lse2));
-          if (masked) {
-            const int kj = kt0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (kj >= L || (CAUSAL && kj > qi)) e = 0.f;
-          }
-          ds[kb * 16 + r] = e * (dp[kb][r] - dd);
-        }
+        for (int r = 0; r < 16; ++r) p[kb * 16 + r] = exp2f_hw(fmaf(s[kb][r], c2, nlq));
+      const bool masked = CAUSAL && kt0 + kTile - 1 > wq0;
+      if (masked) {
+        __builtin_amdgcn_sched_barrier(0);  // keep the mask a branch (diagonal tiles only)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kt0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) > qi) p[kb * 16 + r] = 0.f;
+      }
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const u32x4 sf = {pack2<T>(ds[8 * kc + 0], ds[8 * kc + 1]),
-                          pack2<T>(ds[8 * kc + 2], ds[8 * kc + 3]),
-                          pack2<T>(ds[8 * kc + 4], ds[8 * kc + 5]),
-                          pack2<T>(ds[8 * kc + 6], ds[8 * kc + 7])};
+        float ds[8];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4 ka =
-              *reinterpret_cast<const u32x4*>(&Kt[buf][(db * 32 + l32) * TSTR + 16 * kc + 8 * g]);
-          dqacc[db] = mfma32<T>(ka, sf, dqacc[db]);
+        for (int j = 0; j < 8; ++j) {
+          const int r = 8 * kc + j;
+          ds[j] = p[r] * dp[r >> 4][r & 15];
         }
+        const u32x4 sf = {pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]),
+                          pack2<T>(ds[4], ds[5]), pack2<T>(ds[6], ds[7])};
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dqacc[db] = mfma32<T>(TL::tr_frag(ks, kc * 16, db * 32, lane), sf, dqacc[db]);
       }
     }
-    if (t + 1 < ntiles) lstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
     __syncthreads();
+  };
+
+  TL::load(rk, Ks0, 0, rstride, wave, lane);
+  TL::load(rv, Vs0, 0, rstride, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   // dQ = scale * sum dS k  (signed scale)
@@ -448,8 +463,8 @@ template <int D, class T, bool CAUSAL, bool VARLEN>
 hipError_t launch(const BwdArgs& a, hipStream_t st) {
   const long rows = (long)a.T * a.H;
   constexpr int rows_per_block = kThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_delta_kernel<D, T>), dim3((unsigned)((rows + rows_per_block - 1) /
-                                                                rows_per_block)),
+  hipLaunchKernelGGL((bwd_prep_kernel<D, T>),
+                     dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                      dim3(kThreads), 0, st, a, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -31,7 +31,8 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;  // workspace: D_i = <dO_i, O_i>, fp32, same layout as lse
+  float* neg_delta;  // workspace: -D_i = -<dO_i, O_i>, fp32, same layout as lse
+  float* neg_lse2;   // workspace: -LSE_i * log2(e), fp32, same layout as lse
   const int32_t* cu;
   int B, N, H, T;
   float scale;       // softmax_scale (signed)

@@ -71,8 +71,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: 4 * B * H * N (the fp32 row terms
- * D_i = <dO_i, O_i>). Linear in N: the backward never stores an N x N matrix.
+ * Bytes of device workspace fa_bwd needs: 8 * B * H * N (two fp32 row terms per query:
+ * -D_i = -<dO_i, O_i> and -LSE_i * log2(e)). Linear in N: the backward never stores an
+ * N x N matrix. Returns 0 for arguments fa_bwd would reject as sizes (negative sizes or a
+ * head dim other than 64 or 128).
  */
 size_t fa_bwd_workspace_size(int B, int N, int H, int d);
 
