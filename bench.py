@@ -20,6 +20,11 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --rocprof-summary DB [DB2]   prints a per-kernel table from
                                                      rocprofv3 result databases (kernel
                                                      trace, and counters if collected)
+       python bench.py --traffic-summary FETCH_DB WRITE_DB KERNEL MIB
+                                                    prints the HBM traffic summary of
+                                                    KERNEL from a FETCH_SIZE run and a
+                                                    WRITE_SIZE run that both included a
+                                                    --copy-calibration MIB copy
 """
 import argparse
 import json
@@ -34,6 +39,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak (vendor figure, no sparsity)
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E peak bandwidth (vendor figure)
+CSRC = os.path.join(ROOT, "exact_io_aware_10_amd", "csrc")
+KERNEL_SOURCES = {  # the files whose text determines each kernel's code
+    "fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_internal.h"],
+    "bwd_prep_kernel": ["fa_bwd.hip", "fa_device.h", "fa_internal.h"],
+    "bwd_dkdv_kernel": ["fa_bwd.hip", "fa_device.h", "fa_internal.h"],
+    "bwd_dq_kernel": ["fa_bwd.hip", "fa_device.h", "fa_internal.h"],
+}
 WORKLOAD = dict(name="long_seq_fwd_bwd", B=4, N=8192, H=16, d=128, dtype="bf16", causal=False)
 
 
@@ -47,40 +60,68 @@ def bwd_flops(B, N, H, d, causal):
     return f / 2 if causal else f
 
 
-def cpu_baseline(wl, budget_s=15.0):
-    """fp64 oracle (forward + backward) on a bounded sample of the workload: the first
-    `rows` query rows of one (b, h) slice for the forward, and the backward of one slice
-    at a shortened length. Reported as TFLOP/s of algorithmic work done on the host."""
+def cpu_baseline(wl, bits, min_s=10.0, max_slices=16):
+    """The fp64 oracle timed on the host on a bounded sample of the same workload: whole
+    (b, h) slices of the benchmark's own inputs at full length (forward + backward of each
+    slice is one complete attention problem), repeated until at least `min_s` seconds of
+    host time or `max_slices` slices. Reported as algorithmic TFLOP/s (same FLOP count as
+    the GPU metric)."""
     import oracle
-    from exact_io_aware_10_amd import inputs
 
-    d, dtype = wl["d"], wl["dtype"]
+    d, dtype, causal, N = wl["d"], wl["dtype"], wl["causal"], wl["N"]
     scale = 1 / math.sqrt(d)
     nth = oracle.default_threads()
     w = lambda x: oracle.widen(x, dtype)
-    # forward sample: one full-length (b, h) slice, N keys, all N rows (independent rows)
-    n_fwd = wl["N"]
-    qb, kb, vb, dob = inputs.attention_inputs(1, n_fwd, 1, d, dtype, 0, with_dout=True)
-    q, k, v, do = w(qb), w(kb), w(vb), w(dob)
-    done_flops = 0.0
-    t0 = time.perf_counter()
-    o, lse = oracle.fwd(q, k, v, scale, wl["causal"], nthreads=nth)
-    done_flops += fwd_flops(1, n_fwd, 1, d, wl["causal"])
-    t_fwd = time.perf_counter() - t0
-    # backward sample: one slice at a length that keeps the whole sample near budget_s
-    n_bwd = 2048 if t_fwd > budget_s / 4 else 4096
-    sl = lambda x: np.ascontiguousarray(x[:, :n_bwd])
-    o2, lse2 = oracle.fwd(sl(q), sl(k), sl(v), scale, wl["causal"], nthreads=nth)
-    t1 = time.perf_counter()
-    oracle.bwd(sl(q), sl(k), sl(v), o2, lse2, sl(do), scale, wl["causal"], nthreads=nth)
-    t_bwd = time.perf_counter() - t1
-    done_flops += bwd_flops(1, n_bwd, 1, d, wl["causal"])
-    secs = t_fwd + t_bwd
-    return {"value": round(done_flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": nth,
+    B, H = wl["B"], wl["H"]
+    slices = [(b, h) for b in range(B) for h in range(H)]
+    done = 0
+    secs = 0.0
+    for b, h in slices[:max_slices]:
+        q, k, v, do = (w(np.ascontiguousarray(x[b:b + 1, :, h:h + 1, :])) for x in bits)
+        t0 = time.perf_counter()
+        o, lse = oracle.fwd(q, k, v, scale, causal, nthreads=nth)
+        oracle.bwd(q, k, v, o, lse, do, scale, causal, nthreads=nth)
+        secs += time.perf_counter() - t0
+        done += 1
+        if secs >= min_s:
+            break
+    flops = done * (fwd_flops(1, N, 1, d, causal) + bwd_flops(1, N, 1, d, causal))
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": nth,
             "kind": "oracle",
-            "sample": f"fp64 oracle on one (b,h) slice: forward at N={n_fwd} "
-                      f"({t_fwd:.1f} s) + backward at N={n_bwd} ({t_bwd:.1f} s), d={d}, "
-                      f"same algorithmic FLOP count as the GPU metric"}
+            "sample": f"fp64 oracle forward + backward of {done} of the {B * H} (b,h) slices "
+                      f"of the benchmark's inputs (N={N}, d={d}), {secs:.1f} s on {nth} "
+                      f"host threads"}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    profiles/<kernel>_long_seq_traffic.txt (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the same counter reads for a plain copy of known size), or None when that summary is
+    missing or was taken on other kernel source than the current one."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_long_seq_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k_, v_ = line.split(":", 1)
+                vals[k_.strip()] = v_.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def rocprof_summary(paths):
@@ -92,6 +133,8 @@ def rocprof_summary(paths):
         dbs = (glob.glob(os.path.join(path, "**", "*.db"), recursive=True)
                if os.path.isdir(path) else glob.glob(path))
         for db in sorted(dbs):
+            print(f"# source hash: " + ", ".join(f"{k}={kernel_source_hash(k)}"
+                                                 for k in KERNEL_SOURCES))
             c = sqlite3.connect(db)
             tabs = {r[0] for r in c.execute("select name from sqlite_master")}
             print(f"# {os.path.basename(db)}")
@@ -114,6 +157,46 @@ def rocprof_summary(paths):
                     print(f"  {cn:<32} {val:>16.1f} per dispatch ({n} samples)  {name[:80]}")
 
 
+def _counter_avgs(db_path, counter):
+    """{kernel name: mean per-dispatch value of `counter`} from one rocprofv3 database."""
+    import glob
+    import sqlite3
+    dbs = (glob.glob(os.path.join(db_path, "**", "*.db"), recursive=True)
+           if os.path.isdir(db_path) else [db_path])
+    out = {}
+    for db in dbs:
+        c = sqlite3.connect(db)
+        for name, val in c.execute("select kernel_name, avg(value) from counters_collection "
+                                   "where counter_name = ? group by kernel_name", (counter,)):
+            out[name] = val
+    return out
+
+
+def traffic_summary(fetch_db, write_db, kernel, mib):
+    """HBM bytes per launch of `kernel`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by (known bytes of the calibration copy) / (what the same counter read for it)."""
+    fetch = _counter_avgs(fetch_db, "FETCH_SIZE")
+    write = _counter_avgs(write_db, "WRITE_SIZE")
+    pick = lambda d, key: next(v for k, v in d.items() if key in k)
+    copy_bytes = mib * (1 << 20)
+    f_fetch = copy_bytes / (pick(fetch, "copyBuffer") * 1024)
+    f_write = copy_bytes / (pick(write, "copyBuffer") * 1024)
+    kf, kw = pick(fetch, kernel), pick(write, kernel)
+    total = kf * 1024 * f_fetch + kw * 1024 * f_write
+    print(f"kernel: {kernel}")
+    print(f"kernel_source_sha256_16: {kernel_source_hash(kernel)}")
+    print(f"calibration_copy_bytes: {copy_bytes}")
+    print(f"copy_fetch_size_kib: {pick(fetch, 'copyBuffer'):.1f}")
+    print(f"copy_write_size_kib: {pick(write, 'copyBuffer'):.1f}")
+    print(f"fetch_scale: {f_fetch:.4f}")
+    print(f"write_scale: {f_write:.4f}")
+    print(f"fetch_size_kib_per_dispatch: {kf:.1f}")
+    print(f"write_size_kib_per_dispatch: {kw:.1f}")
+    print(f"hbm_read_bytes_per_launch: {kf * 1024 * f_fetch:.0f}")
+    print(f"hbm_write_bytes_per_launch: {kw * 1024 * f_write:.0f}")
+    print(f"hbm_bytes_per_launch: {total:.0f}")
+
+
 def copy_calibration(mib):
     """One plain device copy of `mib` MiB (reads and writes that many bytes)."""
     import torch
@@ -130,6 +213,11 @@ def copy_calibration(mib):
 def main():
     if "--rocprof-summary" in sys.argv:
         rocprof_summary(sys.argv[sys.argv.index("--rocprof-summary") + 1:])
+        return
+    if "--traffic-summary" in sys.argv:
+        i = sys.argv.index("--traffic-summary")
+        fdb, wdb, kern, mib = sys.argv[i + 1:i + 5]
+        traffic_summary(fdb, wdb, kern, int(mib))
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,28 +248,33 @@ def main():
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     ws = torch.empty(max(fa.fa_bwd_workspace_size(B, N, H, d), 16), dtype=torch.uint8,
                      device=dev)
-    have_bwd = True
+    grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    # the step: forward, then the backward's three stages (exactly what fa_bwd runs), with
+    # an event between launches so each kernel is timed live on the stream it runs on
+    stages = [
+        ("fwd_kernel", lambda: fa.fa_fwd(q, k, v, causal=causal, out=o, lse=lse)),
+        ("bwd_prep_kernel", lambda: fa.fa_bwd_prep(q, k, v, o, lse, do, causal=causal,
+                                                   workspace=ws, grads=grads)),
+        ("bwd_dkdv_kernel", lambda: fa.fa_bwd_dkdv(q, k, v, o, lse, do, causal=causal,
+                                                   workspace=ws, grads=grads)),
+        ("bwd_dq_kernel", lambda: fa.fa_bwd_dq(q, k, v, o, lse, do, causal=causal,
+                                               workspace=ws, grads=grads)),
+    ]
 
     def step(ev=None):
-        nonlocal have_bwd
+        for i, (_, fn) in enumerate(stages):
+            if ev is not None:
+                ev[i].record()
+            fn()
         if ev is not None:
-            ev[0].record()
-        fa.fa_fwd(q, k, v, causal=causal, out=o, lse=lse)
-        if ev is not None:
-            ev[1].record()
-        if have_bwd:
-            try:
-                fa.fa_bwd(q, k, v, o, lse, do, causal=causal, workspace=ws)
-            except fa.FAError:
-                have_bwd = False
-        if ev is not None:
-            ev[2].record()
+            ev[len(stages)].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -189,28 +282,41 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-    ms = sum(step_ms) / len(step_ms)
-    fwd_avg = sum(fwd_ms) / len(fwd_ms)
-    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    avg = lambda xs: sum(xs) / len(xs)
+    kms = {name: avg([e[i].elapsed_time(e[i + 1]) for e in evs])
+           for i, (name, _) in enumerate(stages)}
+    ms = avg([e[0].elapsed_time(e[len(stages)]) for e in evs])
     ff = fwd_flops(B, N, H, d, causal)
-    bf = bwd_flops(B, N, H, d, causal) if have_bwd else 0.0
+    bf = bwd_flops(B, N, H, d, causal)
     tflops = (ff + bf) / (ms * 1e-3) / 1e12
-    fwd_tflops = ff / (fwd_avg * 1e-3) / 1e12
+    fwd_tflops = ff / (kms["fwd_kernel"] * 1e-3) / 1e12
+    bwd_ms = kms["bwd_prep_kernel"] + kms["bwd_dkdv_kernel"] + kms["bwd_dq_kernel"]
 
-    # dominant kernel: the one with the largest share of the step
-    kernels = {"fa_fwd_kernel": (fwd_avg, ff)}
-    if have_bwd:
-        kernels["fa_bwd"] = (bwd_avg, bf)
-    dom = max(kernels, key=lambda n: kernels[n][0])
-    dms, dflops = kernels[dom]
-    achieved = dflops / (dms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "avg_launch_ms": round(dms, 4)}
+    # algorithmic work per launch: the backward's five N x N x d products are S, dP, dV, dK
+    # (all in the dK/dV kernel) and dQ (the dQ kernel's only new product; it recomputes S
+    # and dP); the prep kernel is bandwidth work (reads O, dO, LSE; writes two row terms)
+    work = {
+        "fwd_kernel": ("mfma", ff),
+        "bwd_dkdv_kernel": ("mfma", 0.8 * bf),
+        "bwd_dq_kernel": ("mfma", 0.2 * bf),
+        "bwd_prep_kernel": ("hbm", 2.0 * 2 * B * N * H * d + 4.0 * B * H * N + 8.0 * B * H * N),
+    }
+    per_kernel = {}
+    for name, t in kms.items():
+        bound, amount = work[name]
+        rate = amount / (t * 1e-3)
+        per_kernel[name] = {"ms": round(t, 4), "bound": bound,
+                            ("tflops" if bound == "mfma" else "gbps"):
+                                round(rate / (1e12 if bound == "mfma" else 1e9), 2)}
+    dom = max(kms, key=kms.get)
+    bound, amount = work[dom]
+    if bound == "mfma":
+        achieved, peak, unit = amount / (kms[dom] * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = amount / (kms[dom] * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"
+    roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(dom), "avg_launch_ms": round(kms[dom], 4)}
 
     out = {
         "metric": "attention TFLOP/s fwd+bwd, B4 H16 N8192 d128 bf16 (fwd-only in fwd_tflops)",
@@ -218,16 +324,18 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl["name"], "B": B, "N": N, "H": H, "d": d, "causal": causal,
-                   "step": "fa_fwd + fa_bwd" if have_bwd else "fa_fwd only"},
-        "fwd_tflops": round(fwd_tflops, 2), "fwd_ms": round(fwd_avg, 4),
-        "bwd_ms": round(bwd_avg, 4) if have_bwd else None,
+                   "step": "fa_fwd + fa_bwd (prep, dkdv, dq)"},
+        "fwd_tflops": round(fwd_tflops, 2), "fwd_ms": round(kms["fwd_kernel"], 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "bwd_tflops": round(bf / (bwd_ms * 1e-3) / 1e12, 2),
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_pct_of_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "kernels": per_kernel,
         "wall_s": round(wall, 3),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, bits)
     print(json.dumps(out), flush=True)
 
 

@@ -15,8 +15,9 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_varlen", "fa_bwd_workspace_size", "fa_status_string",
-           "FAError", "library_path", "load_library"]
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen",
+           "fa_bwd_workspace_size", "fa_status_string", "FAError", "library_path",
+           "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libfa_mi355x.so")
@@ -49,8 +50,9 @@ def load_library():
     lib.fa_fwd.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_size.restype = s
-    lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
-    lib.fa_bwd.restype = i
+    for name in ("fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq"):
+        getattr(lib, name).argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
+        getattr(lib, name).restype = i
     lib.fa_fwd_varlen.argtypes = [vp] * 6 + [i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_varlen.restype = i
     _lib = lib
@@ -121,27 +123,59 @@ def fa_fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None):
     return o, lse
 
 
-def fa_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, workspace=None):
-    """Backward attention from the forward's o and lse. Returns (dq, dk, dv)."""
+def _bwd_call(fn, q, k, v, o, lse, dout, causal, softmax_scale, workspace, grads):
     torch = _torch()
     lib = load_library()
     B, N, H, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tensor(name, t, q.shape, q.dtype, q.device)
     _check_tensor("lse", lse, (B, H, N), torch.float32, q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    for name, t in zip(("dq", "dk", "dv"), grads):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
     nbytes = fa_bwd_workspace_size(B, N, H, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
-    rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                    workspace.data_ptr(), B, N, H, d, _dtype_code(q), _scale(softmax_scale, d),
-                    int(bool(causal)), _stream(q.device))
+    dq, dk, dv = grads
+    rc = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), workspace.data_ptr(), B, N, H, d, _dtype_code(q),
+                          _scale(softmax_scale, d), int(bool(causal)), _stream(q.device))
     if rc != FA_OK:
-        raise FAError("fa_bwd", rc)
-    return dq, dk, dv
+        raise FAError(fn, rc)
+    return grads
+
+
+def fa_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None, workspace=None,
+           grads=None):
+    """Backward attention from the forward's o and lse. Returns (dq, dk, dv).
+    grads: optional preallocated (dq, dk, dv)."""
+    return _bwd_call("fa_bwd", q, k, v, o, lse, dout, causal, softmax_scale, workspace, grads)
+
+
+def fa_bwd_prep(q, k, v, o, lse, dout, causal=False, softmax_scale=None, workspace=None,
+                grads=None):
+    """Stage 1 of fa_bwd: row terms into `workspace` (pass the same workspace to the next
+    stages)."""
+    return _bwd_call("fa_bwd_prep", q, k, v, o, lse, dout, causal, softmax_scale, workspace,
+                     grads)
+
+
+def fa_bwd_dkdv(q, k, v, o, lse, dout, causal=False, softmax_scale=None, workspace=None,
+                grads=None):
+    """Stage 2 of fa_bwd: dk and dv (into grads[1], grads[2])."""
+    return _bwd_call("fa_bwd_dkdv", q, k, v, o, lse, dout, causal, softmax_scale, workspace,
+                     grads)
+
+
+def fa_bwd_dq(q, k, v, o, lse, dout, causal=False, softmax_scale=None, workspace=None,
+              grads=None):
+    """Stage 3 of fa_bwd: dq (into grads[0])."""
+    return _bwd_call("fa_bwd_dq", q, k, v, o, lse, dout, causal, softmax_scale, workspace,
+                     grads)
 
 
 def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, softmax_scale=None):

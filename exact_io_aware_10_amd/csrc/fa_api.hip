@@ -85,10 +85,12 @@ FA_EXPORT size_t fa_bwd_workspace_size(int B, int N, int H, int d) {
   return (size_t)8 * B * H * N;
 }
 
-FA_EXPORT fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           void* workspace, int B, int N, int H, int d, fa_dtype dtype,
-                           float softmax_scale, int causal, hipStream_t stream) {
+namespace {
+
+fa_status bwd_common(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                     float softmax_scale, int causal, int stage, hipStream_t stream) {
   fa_status st = check_common(B, N, H, d, dtype, softmax_scale);
   if (st != FA_OK) return st;
   if ((long)B * N * H == 0) return FA_OK;
@@ -115,8 +117,25 @@ FA_EXPORT fa_status fa_bwd(const void* q, const void* k, const void* v, const vo
   a.scale = softmax_scale;
   a.scale_log2 = exp_scale(softmax_scale);
   a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
-  return to_status(fa::launch_bwd(a, d, dtype == FA_BF16, causal != 0, false, stream));
+  return to_status(fa::launch_bwd(a, d, dtype == FA_BF16, causal != 0, false, stage, stream));
 }
+
+}  // namespace
+
+#define FA_BWD_ENTRY(name, stage)                                                          \
+  FA_EXPORT fa_status name(const void* q, const void* k, const void* v, const void* o,    \
+                           const float* lse, const void* dout, void* dq, void* dk,        \
+                           void* dv, void* workspace, int B, int N, int H, int d,         \
+                           fa_dtype dtype, float softmax_scale, int causal,               \
+                           hipStream_t stream) {                                          \
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, N, H, d, dtype,    \
+                      softmax_scale, causal, stage, stream);                              \
+  }
+
+FA_BWD_ENTRY(fa_bwd, fa::kBwdAll)
+FA_BWD_ENTRY(fa_bwd_prep, fa::kBwdPrep)
+FA_BWD_ENTRY(fa_bwd_dkdv, fa::kBwdDkDv)
+FA_BWD_ENTRY(fa_bwd_dq, fa::kBwdDq)
 
 FA_EXPORT fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                                   float* lse, const int32_t* cu_seqlens, int num_seqs,

@@ -460,39 +460,48 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D, class T, bool CAUSAL, bool VARLEN>
-hipError_t launch(const BwdArgs& a, hipStream_t st) {
-  const long rows = (long)a.T * a.H;
-  constexpr int rows_per_block = kThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_prep_kernel<D, T>),
-                     dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                     dim3(kThreads), 0, st, a, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch(const BwdArgs& a, int stage, hipStream_t st) {
+  if (stage == kBwdPrep || stage == kBwdAll) {
+    const long rows = (long)a.T * a.H;
+    constexpr int rows_per_block = kThreads / (D / 8);
+    hipLaunchKernelGGL((bwd_prep_kernel<D, T>),
+                       dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+                       dim3(kThreads), 0, st, a, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const long nblk = (long)((a.N + 127) / 128) * a.H * a.B;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk),
-                     dim3(kThreads), 0, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk),
-                     dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  if (stage == kBwdDkDv || stage == kBwdAll) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk),
+                       dim3(kThreads), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage == kBwdDq || stage == kBwdAll) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk),
+                       dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <int D, class T>
-hipError_t launch_d(const BwdArgs& a, bool causal, bool varlen, hipStream_t st) {
+hipError_t launch_d(const BwdArgs& a, bool causal, bool varlen, int stage, hipStream_t st) {
   if (varlen)
-    return causal ? launch<D, T, true, true>(a, st) : launch<D, T, false, true>(a, st);
-  return causal ? launch<D, T, true, false>(a, st) : launch<D, T, false, false>(a, st);
+    return causal ? launch<D, T, true, true>(a, stage, st) : launch<D, T, false, true>(a, stage, st);
+  return causal ? launch<D, T, true, false>(a, stage, st) : launch<D, T, false, false>(a, stage, st);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, bool varlen,
+hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, bool varlen, int stage,
                       hipStream_t st) {
   if ((long)a.T * a.H == 0) return hipSuccess;
   if (d == 128)
-    return bf16 ? launch_d<128, BF16>(a, causal, varlen, st) : launch_d<128, F16>(a, causal, varlen, st);
-  return bf16 ? launch_d<64, BF16>(a, causal, varlen, st) : launch_d<64, F16>(a, causal, varlen, st);
+    return bf16 ? launch_d<128, BF16>(a, causal, varlen, stage, st)
+                : launch_d<128, F16>(a, causal, varlen, stage, st);
+  return bf16 ? launch_d<64, BF16>(a, causal, varlen, stage, st)
+              : launch_d<64, F16>(a, causal, varlen, stage, st);
 }
 
 }  // namespace fa

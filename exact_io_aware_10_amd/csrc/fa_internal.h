@@ -43,8 +43,10 @@ struct BwdArgs {
 __attribute__((visibility("hidden"))) hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16,
                                                             bool causal, bool varlen,
                                                             hipStream_t stream);
+// Backward stages: row terms, dK/dV, dQ, or all three in that order.
+enum { kBwdPrep = 0, kBwdDkDv = 1, kBwdDq = 2, kBwdAll = 3 };
 __attribute__((visibility("hidden"))) hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16,
-                                                            bool causal, bool varlen,
+                                                            bool causal, bool varlen, int stage,
                                                             hipStream_t stream);
 
 }  // namespace fa

@@ -98,6 +98,29 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  float softmax_scale, int causal, hipStream_t stream);
 
 /*
+ * The three stages fa_bwd runs, in this order, for callers that schedule or time them
+ * separately. Each takes exactly fa_bwd's arguments and validates them the same way.
+ *   fa_bwd_prep : writes the row terms (-D_i and -LSE_i * log2(e)) into workspace; reads
+ *                 o, dout, lse.
+ *   fa_bwd_dkdv : dk and dv; reads q, k, v, dout and the workspace row terms.
+ *   fa_bwd_dq   : dq; reads q, k, v, dout and the workspace row terms.
+ * fa_bwd_dkdv and fa_bwd_dq need the row terms of an fa_bwd_prep call with the same
+ * arguments, completed earlier on the stream (or otherwise ordered before them).
+ */
+fa_status fa_bwd_prep(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                      float softmax_scale, int causal, hipStream_t stream);
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                      float softmax_scale, int causal, hipStream_t stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                    float softmax_scale, int causal, hipStream_t stream);
+
+/*
  * Forward pass over packed sequences (fusion page, 工程实践: pack unequal lengths instead
  * of padding). Sequence s occupies tokens [cu_seqlens[s], cu_seqlens[s+1]) of the packed
  * tensors and is an independent attention problem; the causal mask is relative to the

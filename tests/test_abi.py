@@ -25,7 +25,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_fwd_varlen"])
+        ["fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_prep",
+         "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -76,7 +77,10 @@ def test_bwd_argument_checks(lib):
     assert lib.fa_bwd(*bad, 1, 8, 1, 64, 1, f, 0, None) == 1
     assert lib.fa_bwd(*args, 1, 8, 1, 80, 1, f, 0, None) == 2
     assert lib.fa_bwd(*args, 0, 8, 1, 64, 1, f, 0, None) == 0
-
+    for stage in (lib.fa_bwd_prep, lib.fa_bwd_dkdv, lib.fa_bwd_dq):
+        assert stage(*bad, 1, 8, 1, 64, 1, f, 0, None) == 1
+        assert stage(*args, 1, 8, 1, 80, 1, f, 0, None) == 2
+        assert stage(*args, 1, 8, 1, 64, 1, ctypes.c_float(float("nan")), 0, None) == 1
 
 def test_varlen_argument_checks(lib):
     f = ctypes.c_float(0.1)
