@@ -16,6 +16,7 @@ import math
 import os
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen",
+           "fa_bwd_varlen",
            "fa_bwd_workspace_size", "fa_status_string", "FAError", "library_path",
            "load_library"]
 
@@ -55,6 +56,8 @@ def load_library():
         getattr(lib, name).restype = i
     lib.fa_fwd_varlen.argtypes = [vp] * 6 + [i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_varlen.restype = i
+    lib.fa_bwd_varlen.argtypes = [vp] * 11 + [i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_varlen.restype = i
     _lib = lib
     return lib
 
@@ -199,3 +202,31 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, softmax_scale=N
     if rc != FA_OK:
         raise FAError("fa_fwd_varlen", rc)
     return o, lse
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, causal=False,
+                  softmax_scale=None, workspace=None):
+    """Packed-sequence backward from fa_fwd_varlen's o and lse. Returns (dq, dk, dv);
+    rows of tokens outside every sequence are left as allocated (torch.zeros)."""
+    torch = _torch()
+    lib = load_library()
+    T, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    _check_tensor("lse", lse, (H, T), torch.float32, q.device)
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(q), torch.zeros_like(q)
+    nbytes = fa_bwd_workspace_size(1, T, H, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    rc = lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                           dv.data_ptr(), workspace.data_ptr(), cu_seqlens.data_ptr(),
+                           cu_seqlens.numel() - 1, T, int(max_seqlen), H, d, _dtype_code(q),
+                           _scale(softmax_scale, d), int(bool(causal)), _stream(q.device))
+    if rc != FA_OK:
+        raise FAError("fa_bwd_varlen", rc)
+    return dq, dk, dv

@@ -164,3 +164,41 @@ FA_EXPORT fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, v
   a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
   return to_status(fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, true, stream));
 }
+
+FA_EXPORT fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, void* dq, void* dk,
+                                  void* dv, void* workspace, const int32_t* cu_seqlens,
+                                  int num_seqs, int total_tokens, int max_seqlen, int H, int d,
+                                  fa_dtype dtype, float softmax_scale, int causal,
+                                  hipStream_t stream) {
+  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0) return FA_ERR_INVALID_ARG;
+  fa_status st = check_common(num_seqs, max_seqlen, H, d, dtype, softmax_scale);
+  if (st != FA_OK) return st;
+  if (cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3u)) return FA_ERR_INVALID_ARG;
+  if ((long)num_seqs * max_seqlen * H == 0 || total_tokens == 0) return FA_OK;
+  if (!tensors_ok({q, k, v, o, dout, dq, dk, dv, workspace}) || lse == nullptr ||
+      ((uintptr_t)lse & 3u))
+    return FA_ERR_INVALID_ARG;
+  fa::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.neg_delta = static_cast<float*>(workspace);
+  a.neg_lse2 = a.neg_delta + (long)H * total_tokens;
+  a.cu = cu_seqlens;
+  a.B = num_seqs;
+  a.N = max_seqlen;
+  a.H = H;
+  a.T = total_tokens;
+  a.scale = softmax_scale;
+  a.scale_log2 = exp_scale(softmax_scale);
+  a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
+  return to_status(fa::launch_bwd(a, d, dtype == FA_BF16, causal != 0, true, fa::kBwdAll,
+                                  stream));
+}

@@ -142,6 +142,22 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         int max_seqlen, int H, int d, fa_dtype dtype, float softmax_scale,
                         int causal, hipStream_t stream);
 
+/*
+ * Backward pass over packed sequences: fa_bwd's computation for each sequence of an
+ * fa_fwd_varlen call (same cu_seqlens, max_seqlen, scale and causal flag).
+ *   q, k, v, o, dout : in,  [total_tokens, H, d], dtype
+ *   lse              : in,  fp32 [H, total_tokens] (from fa_fwd_varlen)
+ *   dq, dk, dv       : out, [total_tokens, H, d], dtype; rows of tokens outside every
+ *                      sequence are not written
+ *   workspace        : fa_bwd_workspace_size(1, total_tokens, H, d) bytes, 16-byte aligned
+ * Other arguments, limits and errors as fa_fwd_varlen; deterministic like fa_bwd.
+ */
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* workspace, const int32_t* cu_seqlens, int num_seqs,
+                        int total_tokens, int max_seqlen, int H, int d, fa_dtype dtype,
+                        float softmax_scale, int causal, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

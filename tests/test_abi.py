@@ -26,7 +26,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_prep",
-         "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen"])
+         "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen", "fa_bwd_varlen"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -107,3 +107,15 @@ def test_workspace_is_linear_in_sequence_length(lib):
         assert ws * 1024 <= s_bytes or n < 4096
     assert fa.fa_bwd_workspace_size(4, 4096, 16, 128) == 8 * 4 * 16 * 4096
     assert fa.fa_bwd_workspace_size(1, 8, 1, 96) == 0
+
+
+def test_bwd_varlen_argument_checks(lib):
+    f = ctypes.c_float(0.1)
+    a = [FAKE] * 10
+    assert lib.fa_bwd_varlen(*a, None, 2, 100, 64, 2, 64, 1, f, 1, None) == 1  # no cu_seqlens
+    assert lib.fa_bwd_varlen(*a, FAKE, -1, 100, 64, 2, 64, 1, f, 1, None) == 1
+    assert lib.fa_bwd_varlen(*a, FAKE, 2, 100, 64, 2, 72, 1, f, 1, None) == 2
+    bad = list(a)
+    bad[9] = None  # workspace
+    assert lib.fa_bwd_varlen(*bad, FAKE, 2, 100, 64, 2, 64, 1, f, 1, None) == 1
+    assert lib.fa_bwd_varlen(*a, FAKE, 2, 0, 64, 2, 64, 1, f, 1, None) == 0

@@ -91,3 +91,55 @@ def test_bwd_workload_sampled():
     sum_do = do.sum(axis=1)
     assert np.max(np.abs(sum_dk)) < 0.5, np.max(np.abs(sum_dk))
     assert np.max(np.abs(sum_dv - sum_do)) < 0.5, np.max(np.abs(sum_dv - sum_do))
+
+
+def run_varlen_bwd(lens, H, d, dtype, causal, seed):
+    import torch
+    cu = inputs.cu_seqlens(lens)
+    T = int(cu[-1])
+    print(f"[bwd varlen] nseq={len(lens)} T={T} H={H} d={d} {dtype} causal={causal}",
+          flush=True)
+    bits = [inputs.normal_bits((T, H, d), dtype, seed + i) for i in range(4)]
+    q, k, v, do = (to_device(x, dtype) for x in bits)
+    cu_d = torch.from_numpy(cu).cuda()
+    o, lse = fa().fa_fwd_varlen(q, k, v, cu_d, max(lens), causal=causal)
+    dq, dk, dv = fa().fa_bwd_varlen(q, k, v, o, lse, do, cu_d, max(lens), causal=causal)
+    torch.cuda.synchronize()
+    return cu, bits, [f64_of(t, dtype) for t in (dq, dk, dv)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen_small(d, causal):
+    lens = [5, 1, 130, 64, 300, 0, 17]
+    cu, bits, got = run_varlen_bwd(lens, 3, d, "bf16", causal, seed=21)
+    q, k, v, do = (oracle.widen(x, "bf16") for x in bits)
+    scale = 1 / math.sqrt(d)
+    o, lse = oracle.fwd_varlen(q, k, v, cu, scale, causal)
+    ref = oracle.bwd_varlen(q, k, v, o, lse, do, cu, scale, causal)
+    # short causal sequences (lengths 1, 5, 17) give gradients up to |x| ~ 5, where bf16
+    # output rounding alone costs up to 2^-9 |x|: two half-ulps of relative slack
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert_close(name, g, r, rtol=2.0 ** -7)
+
+
+def test_bwd_varlen_workload_sampled():
+    """The packed causal workload (T = 131072, H16, d128) through forward and backward; the
+    oracle recomputes the shortest sequence, a mid-length one and the last (truncated) one,
+    one head each, as complete problems."""
+    wl = inputs.WORKLOADS["varlen_causal_fwd"]
+    lens = inputs.varlen_lengths(wl.N, *wl.len_range, seed=0)
+    cu, bits, got = run_varlen_bwd(lens, wl.H, wl.d, wl.dtype, wl.causal, seed=0)
+    w = lambda x: oracle.widen(x, wl.dtype)
+    scale = 1 / math.sqrt(wl.d)
+    order = np.argsort(lens)
+    for s, h in sorted({(int(order[0]), 0), (int(order[len(lens) // 3]), 7),
+                        (len(lens) - 1, wl.H - 1)}):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = lambda x: x[a:b, h:h + 1, :][None]
+        q, k, v, do = (w(sl(x)) for x in bits)
+        o, lse = oracle.fwd(q, k, v, scale, wl.causal)
+        ref = oracle.bwd(q, k, v, o, lse, do, scale, wl.causal)
+        print(f"  seq {s} len {b - a} head {h}", flush=True)
+        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+            assert_close(name, g[a:b, h:h + 1][None], r)
