@@ -41,11 +41,14 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak (vendor figure, no sparsity)
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E peak bandwidth (vendor figure)
 CSRC = os.path.join(ROOT, "exact_io_aware_10_amd", "csrc")
-KERNEL_SOURCES = {  # the files whose text determines each kernel's code
-    "fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_internal.h"],
-    "bwd_prep_kernel": ["fa_bwd.hip", "fa_device.h", "fa_internal.h"],
-    "bwd_dkdv_kernel": ["fa_bwd.hip", "fa_device.h", "fa_internal.h"],
-    "bwd_dq_kernel": ["fa_bwd.hip", "fa_device.h", "fa_internal.h"],
+KERNEL_SOURCES = {  # the files whose text determines each kernel's code (build.py: flags)
+    "fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_internal.h", "../build.py"],
+    "bwd_prep_kernel": ["fa_bwd.hip", "fa_bwd_common.h", "fa_device.h", "fa_internal.h",
+                        "../build.py"],
+    "bwd_dkdv_kernel": ["fa_bwd_dkdv.hip", "fa_bwd_common.h", "fa_device.h", "fa_internal.h",
+                        "../build.py"],
+    "bwd_dq_kernel": ["fa_bwd_dq.hip", "fa_bwd_common.h", "fa_device.h", "fa_internal.h",
+                      "../build.py"],
 }
 WORKLOAD = dict(name="long_seq_fwd_bwd", B=4, N=8192, H=16, d=128, dtype="bf16", causal=False)
 

@@ -2,6 +2,9 @@
 
 Every .hip file under csrc/ is compiled to an object in parallel, then linked into
 exact_io_aware_10_amd/libfa_mi355x.so. Usage: python -m exact_io_aware_10_amd.build [-v]
+
+Environment (optional): FA_EXTRA_CFLAGS (extra hipcc flags for every file), FA_LIB_OUT
+(output library path), FA_BUILD_DIR (object directory).
 """
 import os
 import subprocess
@@ -11,8 +14,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-BUILD_DIR = os.path.join(ROOT, "_build")
-LIB = os.path.join(HERE, "libfa_mi355x.so")
+BUILD_DIR = os.environ.get("FA_BUILD_DIR") or os.path.join(ROOT, "_build")
+LIB = os.environ.get("FA_LIB_OUT") or os.path.join(HERE, "libfa_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -22,7 +25,15 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-result",
-]
+] + os.environ.get("FA_EXTRA_CFLAGS", "").split()
+
+# Per-file flags. The dQ kernel's softmax-side VALU work reads the S and dP accumulators
+# directly, so its MFMA results are kept in VGPRs (in AGPRs they would be copied back for
+# every tile); the dK/dV kernel keeps the default (its 128 gradient accumulators live in
+# AGPRs).
+FILE_FLAGS = {
+    "fa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def sources():
@@ -31,7 +42,7 @@ def sources():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -28,63 +28,11 @@
 // 16-byte chunks of row r are XOR-swizzled by f(r) = ((r&3)<<2)|((r>>2)&3) (d = 128), which
 // makes both read patterns conflict-free.
 // -D is loaded as the initial value of the dP accumulators, so dS = P * acc.
-#include <type_traits>
-
-#include "fa_device.h"
-#include "fa_internal.h"
+#include "fa_bwd_common.h"
 
 namespace fa {
+namespace bwd {
 namespace {
-
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 64;  // rows of the streamed tile (queries in dK/dV, keys in dQ)
-constexpr float kLog2e = 1.44269504088896340736f;
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Chunk swizzle of tile row r, good for both row and transposed fragment reads.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-// Per-slice addressing shared by the kernels.
-struct SliceInfo {
-  long tok0;  // first token of the slice in the [tokens, H, d] tensors
-  int L;      // rows in the slice
-  long stat;  // offset of row 0 of the slice in lse / the workspace row terms
-};
-
-__device__ __forceinline__ SliceInfo slice_info(const BwdArgs& a, int bs, int h) {
-  SliceInfo s;
-  if (a.cu != nullptr) {
-    int s0 = a.cu[bs], s1 = a.cu[bs + 1];
-    s0 = s0 < 0 ? 0 : (s0 > a.T ? a.T : s0);
-    s1 = s1 < s0 ? s0 : (s1 > a.T ? a.T : s1);
-    s.L = s1 - s0 < a.N ? s1 - s0 : a.N;
-    s.tok0 = s0;
-    s.stat = (long)h * a.T + s0;
-  } else {
-    s.L = a.N;
-    s.tok0 = (long)bs * a.N;
-    s.stat = ((long)bs * a.H + h) * a.N;
-  }
-  return s;
-}
-
-// Work item of a dense or packed launch: (block index within the slice, head, batch/seq).
-__device__ __forceinline__ void decode_work(const BwdArgs& a, int nblk, bool varlen, int& blk,
-                                            int& h, int& bs) {
-  uint32_t w = blockIdx.x;
-  if (!varlen) w = xcd_remap(w, gridDim.x);
-  blk = w % nblk;
-  h = (w / nblk) % a.H;
-  bs = w / (nblk * a.H);
-}
 
 // ---------------------------------------------------------------- 1. row terms
 // ws[0 .. rows) = -D_i = -<dO_i, O_i>;  ws[rows .. 2 rows) = -LSE_i * log2(e)
@@ -122,386 +70,35 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a, long rows
   }
 }
 
-// ---------------------------------------------------------------- tile access helpers
-template <int D>
-struct Tile {
-  static constexpr int ROWB = D * 2;        // bytes per row
-  static constexpr int CPR = D / 8;         // 16-byte chunks per row
-  static constexpr int BYTES = kTile * ROWB;
-  static constexpr int RPL = 1024 / ROWB;   // rows per 1 KiB direct load
-  static constexpr int LPW = BYTES / 1024 / kWaves;  // direct loads per wave per tile
-
-  // direct HBM/L2 -> LDS load of tile rows [row0, row0 + kTile) of a [tokens, H, D] tensor
-  static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint8_t* tile,
-                                              int row0, uint32_t rstride, int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int blk = wave * LPW + j;
-      const int row = blk * RPL + lane / CPR;
-      const int c = (lane % CPR) ^ swz<D>(row);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + blk * 1024), 16,
-                                               (uint32_t)(row0 + row) * rstride + c * 16, 0,
-                                               0, 0);
-    }
-  }
-  // row fragment: row r, logical chunk c (16 bytes)
-  static __device__ __forceinline__ u32x4 row_frag(const uint8_t* tile, int r, int c) {
-    return *reinterpret_cast<const u32x4*>(tile + r * ROWB + ((c ^ swz<D>(r)) << 4));
-  }
-  // transposed fragment (A operand of a 32x32x16 MFMA over 16 tile rows k0..k0+15 and 32
-  // tile columns d0..d0+31): lane (l32, g) gets column d0 + l32 of rows
-  // k0 + 4g + {0,1,2,3} and k0 + 8 + 4g + {0,1,2,3}, matching the row order of P / dS
-  // registers taken from a 32x32 accumulator.
-  static __device__ __forceinline__ u32x4 tr_frag(const uint8_t* tile, int k0, int d0, int lane) {
-    const int i16 = lane & 15, G = (lane >> 4) & 1, g = lane >> 5;
-    const int r = k0 + 4 * g + (i16 >> 2);
-    const int c = (d0 >> 3) + 2 * G + ((i16 & 3) >> 1);
-    const int half = 8 * (i16 & 1);
-    const uint8_t* p0 = tile + r * ROWB + ((c ^ swz<D>(r)) << 4) + half;
-    const uint8_t* p1 = tile + (r + 8) * ROWB + ((c ^ swz<D>(r + 8)) << 4) + half;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
-    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-    return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-  }
-};
-
-// ---------------------------------------------------------------- 2. dK, dV
-template <int D, class T, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int BKV = 32 * kWaves;  // keys per workgroup
-  constexpr int DC = D / 16, DB = D / 32;
-  using TL = Tile<D>;
-
-  __shared__ __attribute__((aligned(1024))) uint8_t Qs0[TL::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Qs1[TL::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t dOs0[TL::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t dOs1[TL::BYTES];
-  __shared__ __attribute__((aligned(256))) float nl0[kTile];  // -LSE log2(e)
-  __shared__ __attribute__((aligned(256))) float nl1[kTile];
-  __shared__ __attribute__((aligned(256))) float nd0[kTile];  // -D
-  __shared__ __attribute__((aligned(256))) float nd1[kTile];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nkb = (a.N + BKV - 1) / BKV;
-  int kb, h, bs;
-  decode_work(a, nkb, VARLEN, kb, h, bs);
-  const SliceInfo si = slice_info(a, bs, h);
-  const int L = si.L;
-  const int k0 = kb * BKV;
-  if (k0 >= L) return;
-
-  const uint32_t rstride = (uint32_t)a.H * D * 2;
-  const long base = (si.tok0 * a.H + h) * D;
-  const uint32_t nbytes = (uint32_t)(L - 1) * rstride + D * 2;
-  const auto rq = make_rsrc(a.q + base, nbytes);
-  const auto rk = make_rsrc(a.k + base, nbytes);
-  const auto rv = make_rsrc(a.v + base, nbytes);
-  const auto rdo = make_rsrc(a.dout + base, nbytes);
-  const auto rdk = make_rsrc(a.dk + base, nbytes);
-  const auto rdv = make_rsrc(a.dv + base, nbytes);
-  const auto rnl = make_rsrc(a.neg_lse2 + si.stat, (uint32_t)L * 4);
-  const auto rnd = make_rsrc(a.neg_delta + si.stat, (uint32_t)L * 4);
-
-  const int wk0 = k0 + wave * 32;  // this wave's keys: wk0 .. wk0+31
-  const int key = wk0 + l32;       // the key this lane's accumulators belong to
-
-  // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T. A negative
-  // softmax scale is folded into K's sign (the gradient below then uses the signed scale).
-  u32x4 kreg[DC], vreg[DC];
-#pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    kreg[dc] = buf_load16(rk, (uint32_t)key * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
-    vreg[dc] = buf_load16(rv, (uint32_t)key * rstride + (16 * dc + 8 * g) * 2);
-  }
-
-  f32x16 dkacc[DB], dvacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dkacc[db] = dvacc[db] = f32x16{};
-
-  const int qt_begin = CAUSAL ? k0 / kTile : 0;
-  const int qt_end = (L + kTile - 1) / kTile;
-  const float c2 = a.scale_log2;
-
-  auto load_tile = [&](int qt, uint8_t* qs, uint8_t* dos, float* nl, float* nd) {
-    TL::load(rq, qs, qt * kTile, rstride, wave, lane);
-    TL::load(rdo, dos, qt * kTile, rstride, wave, lane);
-    if (wave == 0) {  // 64 lanes x 4 bytes: one row term per query of the tile
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rnl, (lds_void*)nl, 4, (qt * kTile + lane) * 4,
-                                               0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rnd, (lds_void*)nd, 4, (qt * kTile + lane) * 4,
-                                               0, 0, 0);
-    }
-  };
-
-  auto step = [&](auto bsel, int qt) {
-    constexpr int B = decltype(bsel)::value;
-    const uint8_t* qs = B ? Qs1 : Qs0;
-    const uint8_t* dos = B ? dOs1 : dOs0;
-    const float* nl = B ? nl1 : nl0;
-    const float* nd = B ? nd1 : nd0;
-    if (qt + 1 < qt_end) load_tile(qt + 1, B ? Qs0 : Qs1, B ? dOs0 : dOs1, B ? nl0 : nl1,
-                                   B ? nd0 : nd1);
-    const int q0 = qt * kTile;
-    const bool active = !CAUSAL || q0 + kTile - 1 >= wk0;
-    if (active) {
-      const bool diag = CAUSAL && q0 < wk0 + 31;
-      // the two 32-query halves of the tile, one after the other
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // S (queries x keys) and dP - D (the accumulator starts at -D of each query)
-        f32x16 s = f32x16{}, dp;
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&nd[qb * 32 + 8 * a4 + 4 * g]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dp[4 * a4 + j] = d4[j];
-        }
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          s = mfma32<T>(TL::row_frag(qs, qb * 32 + l32, 2 * dc + g), kreg[dc], s);
-          dp = mfma32<T>(TL::row_frag(dos, qb * 32 + l32, 2 * dc + g), vreg[dc], dp);
-        }
-        float p[16];
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&nl[qb * 32 + 8 * a4 + 4 * g]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p[4 * a4 + j] = exp2f_hw(fmaf(s[4 * a4 + j], c2, l4[j]));
-        }
-        if (diag) {
-          __builtin_amdgcn_sched_barrier(0);  // keep the mask a branch (diagonal tiles only)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key > q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) p[r] = 0.f;
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          float ds[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ds[j] = p[8 * hh + j] * dp[8 * hh + j];
-          const u32x4 pf = {pack2<T>(p[8 * hh + 0], p[8 * hh + 1]),
-                            pack2<T>(p[8 * hh + 2], p[8 * hh + 3]),
-                            pack2<T>(p[8 * hh + 4], p[8 * hh + 5]),
-                            pack2<T>(p[8 * hh + 6], p[8 * hh + 7])};
-          const u32x4 sf = {pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]),
-                            pack2<T>(ds[4], ds[5]), pack2<T>(ds[6], ds[7])};
-          // dV^T += dO^T P and dK^T += Q^T dS over the 16-query chunk 2 qb + hh
-          const int kc = 2 * qb + hh;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            dvacc[db] = mfma32<T>(TL::tr_frag(dos, kc * 16, db * 32, lane), pf, dvacc[db]);
-            dkacc[db] = mfma32<T>(TL::tr_frag(qs, kc * 16, db * 32, lane), sf, dkacc[db]);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
-    __syncthreads();
-  };
-
-  load_tile(qt_begin, Qs0, dOs0, nl0, nd0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int qt = qt_begin; qt < qt_end; qt += 2) {
-    step(std::integral_constant<int, 0>{}, qt);
-    if (qt + 1 < qt_end) step(std::integral_constant<int, 1>{}, qt + 1);
-  }
-
-  // dK = scale * sum dS q (signed scale), dV = sum P dO
-  const float ks = a.scale;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const uint32_t off = (uint32_t)key * rstride + (db * 32 + 8 * rr + 4 * g) * 2;
-      const f32x16& x = dkacc[db];
-      const f32x16& y = dvacc[db];
-      buf_store8(rdk, off, u32x2{pack2<T>(x[4 * rr] * ks, x[4 * rr + 1] * ks),
-                                 pack2<T>(x[4 * rr + 2] * ks, x[4 * rr + 3] * ks)});
-      buf_store8(rdv, off, u32x2{pack2<T>(y[4 * rr], y[4 * rr + 1]),
-                                 pack2<T>(y[4 * rr + 2], y[4 * rr + 3])});
-    }
-}
-
-// ---------------------------------------------------------------- 3. dQ
-template <int D, class T, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BQ = 32 * kWaves;
-  constexpr int DC = D / 16, DB = D / 32;
-  using TL = Tile<D>;
-
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks0[TL::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks1[TL::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs0[TL::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs1[TL::BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nqb = (a.N + BQ - 1) / BQ;
-  int qb, h, bs;
-  decode_work(a, nqb, VARLEN, qb, h, bs);
-  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
-  const SliceInfo si = slice_info(a, bs, h);
-  const int L = si.L;
-  const int q0 = qb * BQ;
-  if (q0 >= L) return;
-
-  const uint32_t rstride = (uint32_t)a.H * D * 2;
-  const long base = (si.tok0 * a.H + h) * D;
-  const uint32_t nbytes = (uint32_t)(L - 1) * rstride + D * 2;
-  const auto rq = make_rsrc(a.q + base, nbytes);
-  const auto rk = make_rsrc(a.k + base, nbytes);
-  const auto rv = make_rsrc(a.v + base, nbytes);
-  const auto rdo = make_rsrc(a.dout + base, nbytes);
-  const auto rdq = make_rsrc(a.dq + base, nbytes);
-
-  const int wq0 = q0 + wave * 32;
-  const int qi = wq0 + l32;  // the query row of this lane
-  u32x4 qreg[DC], doreg[DC];
-#pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    qreg[dc] = buf_load16(rq, (uint32_t)qi * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
-    doreg[dc] = buf_load16(rdo, (uint32_t)qi * rstride + (16 * dc + 8 * g) * 2);
-  }
-  const float nlq = qi < L ? a.neg_lse2[si.stat + qi] : 0.f;
-  const float ndq = qi < L ? a.neg_delta[si.stat + qi] : 0.f;
-
-  f32x16 dqacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dqacc[db] = f32x16{};
-
-  const int kend = CAUSAL ? (L < q0 + BQ ? L : q0 + BQ) : L;
-  const int ntiles = (kend + kTile - 1) / kTile;
-  const float c2 = a.scale_log2;
-
-  auto step = [&](auto bsel, int t) {
-    constexpr int B = decltype(bsel)::value;
-    const uint8_t* ks = B ? Ks1 : Ks0;
-    const uint8_t* vs = B ? Vs1 : Vs0;
-    if (t + 1 < ntiles) {
-      TL::load(rk, B ? Ks0 : Ks1, (t + 1) * kTile, rstride, wave, lane);
-      TL::load(rv, B ? Vs0 : Vs1, (t + 1) * kTile, rstride, wave, lane);
-    }
-    const int kt0 = t * kTile;
-    const bool active = !CAUSAL || kt0 <= wq0 + 31;
-    if (active) {
-      // S^T and dP^T - D (keys x queries), two 32-key blocks
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[kb][r] = ndq;
-      }
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = mfma32<T>(TL::row_frag(ks, kb * 32 + l32, 2 * dc + g), qreg[dc], s[kb]);
-          dp[kb] = mfma32<T>(TL::row_frag(vs, kb * 32 + l32, 2 * dc + g), doreg[dc], dp[kb]);
-        }
-      float p[32];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[kb * 16 + r] = exp2f_hw(fmaf(s[kb][r], c2, nlq));
-      const bool masked = CAUSAL && kt0 + kTile - 1 > wq0;
-      if (masked) {
-        __builtin_amdgcn_sched_barrier(0);  // keep the mask a branch (diagonal tiles only)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kt0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) > qi) p[kb * 16 + r] = 0.f;
-      }
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        float ds[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * kc + j;
-          ds[j] = p[r] * dp[r >> 4][r & 15];
-        }
-        const u32x4 sf = {pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]),
-                          pack2<T>(ds[4], ds[5]), pack2<T>(ds[6], ds[7])};
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dqacc[db] = mfma32<T>(TL::tr_frag(ks, kc * 16, db * 32, lane), sf, dqacc[db]);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
-    __syncthreads();
-  };
-
-  TL::load(rk, Ks0, 0, rstride, wave, lane);
-  TL::load(rv, Vs0, 0, rstride, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
-  }
-
-  // dQ = scale * sum dS k  (signed scale)
-  const float qs = a.scale;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const f32x16& x = dqacc[db];
-      buf_store8(rdq, (uint32_t)qi * rstride + (db * 32 + 8 * rr + 4 * g) * 2,
-                 u32x2{pack2<T>(x[4 * rr] * qs, x[4 * rr + 1] * qs),
-                       pack2<T>(x[4 * rr + 2] * qs, x[4 * rr + 3] * qs)});
-    }
-}
-
-template <int D, class T, bool CAUSAL, bool VARLEN>
-hipError_t launch(const BwdArgs& a, int stage, hipStream_t st) {
-  if (stage == kBwdPrep || stage == kBwdAll) {
-    const long rows = (long)a.T * a.H;
-    constexpr int rows_per_block = kThreads / (D / 8);
-    hipLaunchKernelGGL((bwd_prep_kernel<D, T>),
-                       dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                       dim3(kThreads), 0, st, a, rows);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const long nblk = (long)((a.N + 127) / 128) * a.H * a.B;
-  if (stage == kBwdDkDv || stage == kBwdAll) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk),
-                       dim3(kThreads), 0, st, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (stage == kBwdDq || stage == kBwdAll) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk),
-                       dim3(kThreads), 0, st, a);
-    return hipGetLastError();
-  }
-  return hipSuccess;
-}
-
 template <int D, class T>
-hipError_t launch_d(const BwdArgs& a, bool causal, bool varlen, int stage, hipStream_t st) {
-  if (varlen)
-    return causal ? launch<D, T, true, true>(a, stage, st) : launch<D, T, false, true>(a, stage, st);
-  return causal ? launch<D, T, true, false>(a, stage, st) : launch<D, T, false, false>(a, stage, st);
+hipError_t launch_prep(const BwdArgs& a, hipStream_t st) {
+  const long rows = (long)a.T * a.H;
+  constexpr int rows_per_block = kThreads / (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<D, T>),
+                     dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+                     dim3(kThreads), 0, st, a, rows);
+  return hipGetLastError();
 }
 
 }  // namespace
+}  // namespace bwd
 
 hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, bool varlen, int stage,
                       hipStream_t st) {
   if ((long)a.T * a.H == 0) return hipSuccess;
-  if (d == 128)
-    return bf16 ? launch_d<128, BF16>(a, causal, varlen, stage, st)
-                : launch_d<128, F16>(a, causal, varlen, stage, st);
-  return bf16 ? launch_d<64, BF16>(a, causal, varlen, stage, st)
-              : launch_d<64, F16>(a, causal, varlen, stage, st);
+  if (stage == kBwdPrep || stage == kBwdAll) {
+    const hipError_t e = d == 128 ? (bf16 ? bwd::launch_prep<128, BF16>(a, st)
+                                          : bwd::launch_prep<128, F16>(a, st))
+                                  : (bf16 ? bwd::launch_prep<64, BF16>(a, st)
+                                          : bwd::launch_prep<64, F16>(a, st));
+    if (e != hipSuccess) return e;
+  }
+  if (stage == kBwdDkDv || stage == kBwdAll) {
+    const hipError_t e = bwd::launch_dkdv(a, d, bf16, causal, varlen, st);
+    if (e != hipSuccess) return e;
+  }
+  if (stage == kBwdDq || stage == kBwdAll) return bwd::launch_dq(a, d, bf16, causal, varlen, st);
+  return hipSuccess;
 }
 
 }  // namespace fa

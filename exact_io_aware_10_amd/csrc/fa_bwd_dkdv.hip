@@ -1,0 +1,199 @@
+// dK/dV kernel of the backward pass (see fa_bwd.hip for the gradient formulas): one
+// workgroup per 128-key block, 32 keys per wave with K and V in registers; streams 64-query
+// tiles of Q, dO and the row terms from HBM/L2 straight into LDS, double buffered.
+// S = Q K^T and dP = dO V^T are computed with lanes <-> keys, so P and dS leave the
+// accumulators in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS.
+#include "fa_bwd_common.h"
+
+namespace fa {
+namespace bwd {
+namespace {
+
+template <int D, class T, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BKV = 32 * kWaves;  // keys per workgroup
+  constexpr int DC = D / 16, DB = D / 32;
+  using TL = Tile<D>;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t Qs0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Qs1[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dOs0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dOs1[TL::BYTES];
+  __shared__ __attribute__((aligned(256))) float nl0[kTile];  // -LSE log2(e)
+  __shared__ __attribute__((aligned(256))) float nl1[kTile];
+  __shared__ __attribute__((aligned(256))) float nd0[kTile];  // -D
+  __shared__ __attribute__((aligned(256))) float nd1[kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  Lanes<D> ln(lane);
+  const int nkb = (a.N + BKV - 1) / BKV;
+  int kb, h, bs;
+  decode_work(a, nkb, VARLEN, kb, h, bs);
+  const SliceInfo si = slice_info(a, bs, h);
+  const int L = si.L;
+  const int k0 = kb * BKV;
+  if (k0 >= L) return;
+
+  const uint32_t rstride = (uint32_t)a.H * D * 2;
+  const long base = (si.tok0 * a.H + h) * D;
+  const uint32_t nbytes = (uint32_t)(L - 1) * rstride + D * 2;
+  const auto rq = make_rsrc(a.q + base, nbytes);
+  const auto rk = make_rsrc(a.k + base, nbytes);
+  const auto rv = make_rsrc(a.v + base, nbytes);
+  const auto rdo = make_rsrc(a.dout + base, nbytes);
+  const auto rdk = make_rsrc(a.dk + base, nbytes);
+  const auto rdv = make_rsrc(a.dv + base, nbytes);
+  const auto rnl = make_rsrc(a.neg_lse2 + si.stat, (uint32_t)L * 4);
+  const auto rnd = make_rsrc(a.neg_delta + si.stat, (uint32_t)L * 4);
+
+  const int wk0 = k0 + wave * 32;  // this wave's keys: wk0 .. wk0+31
+  const int key = wk0 + l32;       // the key this lane's accumulators belong to
+
+  // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T. A negative
+  // softmax scale is folded into K's sign (the gradient below then uses the signed scale).
+  u32x4 kreg[DC], vreg[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) {
+    kreg[dc] = buf_load16(rk, (uint32_t)key * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
+    vreg[dc] = buf_load16(rv, (uint32_t)key * rstride + (16 * dc + 8 * g) * 2);
+  }
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dkacc[db] = dvacc[db] = f32x16{};
+
+  const int qt_begin = CAUSAL ? k0 / kTile : 0;
+  const int qt_end = (L + kTile - 1) / kTile;
+  const float c2 = a.scale_log2;
+
+  auto load_tile = [&](int qt, uint8_t* qs, uint8_t* dos, float* nl, float* nd) {
+    TL::load(rq, qs, qt * kTile, rstride, wave, lane);
+    TL::load(rdo, dos, qt * kTile, rstride, wave, lane);
+    if (wave == 0) {  // 64 lanes x 4 bytes: one row term per query of the tile
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rnl, (lds_void*)nl, 4, (qt * kTile + lane) * 4,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rnd, (lds_void*)nd, 4, (qt * kTile + lane) * 4,
+                                               0, 0, 0);
+    }
+  };
+
+  auto step = [&](auto bsel, int qt) {
+    constexpr int B = decltype(bsel)::value;
+    const uint8_t* qs = B ? Qs1 : Qs0;
+    const uint8_t* dos = B ? dOs1 : dOs0;
+    const float* nl = B ? nl1 : nl0;
+    const float* nd = B ? nd1 : nd0;
+    if (qt + 1 < qt_end) load_tile(qt + 1, B ? Qs0 : Qs1, B ? dOs0 : dOs1, B ? nl0 : nl1,
+                                   B ? nd0 : nd1);
+    const int q0 = qt * kTile;
+    const bool active = !CAUSAL || q0 + kTile - 1 >= wk0;
+    if (active) {
+      const bool diag = CAUSAL && q0 < wk0 + 31;
+      // the two 32-query halves of the tile, one after the other
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        ln.refresh();
+        // S (queries x keys) and dP - D (the accumulator starts at -D of each query)
+        f32x16 s = f32x16{}, dp;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&nd[qb * 32 + 8 * a4 + 4 * g]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dp[4 * a4 + j] = d4[j];
+        }
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          s = mfma32<T>(ln.row_frag(qs, qb * 32, dc), kreg[dc], s);
+          dp = mfma32<T>(ln.row_frag(dos, qb * 32, dc), vreg[dc], dp);
+        }
+        float p[16];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&nl[qb * 32 + 8 * a4 + 4 * g]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[4 * a4 + j] = exp2f_hw(fmaf(s[4 * a4 + j], c2, l4[j]));
+        }
+        if (diag) {
+          __builtin_amdgcn_sched_barrier(0);  // keep the mask a branch (diagonal tiles only)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key > q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) p[r] = 0.f;
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float ds[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ds[j] = p[8 * hh + j] * dp[8 * hh + j];
+          const u32x4 pf = {pack2<T>(p[8 * hh + 0], p[8 * hh + 1]),
+                            pack2<T>(p[8 * hh + 2], p[8 * hh + 3]),
+                            pack2<T>(p[8 * hh + 4], p[8 * hh + 5]),
+                            pack2<T>(p[8 * hh + 6], p[8 * hh + 7])};
+          const u32x4 sf = {pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]),
+                            pack2<T>(ds[4], ds[5]), pack2<T>(ds[6], ds[7])};
+          // dV^T += dO^T P and dK^T += Q^T dS over the 16-query chunk 2 qb + hh
+          const int kc = 2 * qb + hh;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dvacc[db] = mfma32<T>(ln.tr_frag(dos, kc * 16, db), pf, dvacc[db]);
+            dkacc[db] = mfma32<T>(ln.tr_frag(qs, kc * 16, db), sf, dkacc[db]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
+    __syncthreads();
+  };
+
+  load_tile(qt_begin, Qs0, dOs0, nl0, nd0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int qt = qt_begin; qt < qt_end; qt += 2) {
+    step(std::integral_constant<int, 0>{}, qt);
+    if (qt + 1 < qt_end) step(std::integral_constant<int, 1>{}, qt + 1);
+  }
+
+  // dK = scale * sum dS q (signed scale), dV = sum P dO
+  const float ks = a.scale;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const uint32_t off = (uint32_t)key * rstride + (db * 32 + 8 * rr + 4 * g) * 2;
+      const f32x16& x = dkacc[db];
+      const f32x16& y = dvacc[db];
+      buf_store8(rdk, off, u32x2{pack2<T>(x[4 * rr] * ks, x[4 * rr + 1] * ks),
+                                 pack2<T>(x[4 * rr + 2] * ks, x[4 * rr + 3] * ks)});
+      buf_store8(rdv, off, u32x2{pack2<T>(y[4 * rr], y[4 * rr + 1]),
+                                 pack2<T>(y[4 * rr + 2], y[4 * rr + 3])});
+    }
+}
+
+
+template <int D, class T, bool CAUSAL, bool VARLEN>
+hipError_t launch_t(const BwdArgs& a, hipStream_t st) {
+  const long nblk = (long)((a.N + 127) / 128) * a.H * a.B;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(kThreads), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+template <int D, class T>
+hipError_t launch_c(const BwdArgs& a, bool causal, bool varlen, hipStream_t st) {
+  if (varlen)
+    return causal ? launch_t<D, T, true, true>(a, st) : launch_t<D, T, false, true>(a, st);
+  return causal ? launch_t<D, T, true, false>(a, st) : launch_t<D, T, false, false>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_dkdv(const BwdArgs& a, int d, bool bf16, bool causal, bool varlen,
+                       hipStream_t st) {
+  if (d == 128)
+    return bf16 ? launch_c<128, BF16>(a, causal, varlen, st) : launch_c<128, F16>(a, causal, varlen, st);
+  return bf16 ? launch_c<64, BF16>(a, causal, varlen, st) : launch_c<64, F16>(a, causal, varlen, st);
+}
+
+}  // namespace bwd
+}  // namespace fa
