@@ -12,12 +12,13 @@
 //
 // Three launches, no floating-point atomics (bitwise deterministic):
 //   1. bwd_prep_kernel : per row, -D_i and -LSE_i log2(e) into the workspace.
-//   2. bwd_dkdv_kernel : one workgroup per 128-key block (32 keys per wave; K and V held
-//                        in registers); streams 64-query tiles of Q, dO and the two row
-//                        terms from HBM/L2 straight into LDS, double buffered.
-//                        S = Q K^T and dP = dO V^T are computed with lanes <-> keys, so P
-//                        and dS leave the accumulators in the B-operand layout of
-//                        dV^T += dO^T P and dK^T += Q^T dS.
+//   2. bwd_dkdv_kernel : one workgroup of 8 waves per 128-key block; wave (kg, qh) owns 32
+//                        keys (K in registers, V of the block in LDS) and one 32-query half
+//                        of each 64-query tile of Q, dO and the two row terms, streamed from
+//                        HBM/L2 straight into LDS, double buffered. S = Q K^T and dP = dO V^T
+//                        are computed with lanes <-> keys, so P and dS leave the accumulators
+//                        in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS; the two
+//                        halves' partial dK, dV are summed through LDS at the end.
 //   3. bwd_dq_kernel   : one workgroup per 128-query block (32 queries per wave; Q and dO
 //                        in registers); streams 64-key tiles of K and V; S^T and dP^T with
 //                        lanes <-> queries feed dQ^T += K^T dS^T.

@@ -63,13 +63,13 @@ __device__ __forceinline__ void decode_work(const BwdArgs& a, int nblk, bool var
 }
 
 // ---------------------------------------------------------------- tile access helpers
-template <int D>
+template <int D, int NW = kWaves>
 struct Tile {
   static constexpr int ROWB = D * 2;        // bytes per row
   static constexpr int CPR = D / 8;         // 16-byte chunks per row
   static constexpr int BYTES = kTile * ROWB;
   static constexpr int RPL = 1024 / ROWB;   // rows per 1 KiB direct load
-  static constexpr int LPW = BYTES / 1024 / kWaves;  // direct loads per wave per tile
+  static constexpr int LPW = BYTES / 1024 / NW;  // direct loads per wave per tile (NW waves)
 
   // direct HBM/L2 -> LDS load of tile rows [row0, row0 + kTile) of a [tokens, H, D] tensor
   static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint8_t* tile,

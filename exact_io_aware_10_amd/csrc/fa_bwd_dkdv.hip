@@ -1,6 +1,6 @@
 // dK/dV kernel of the backward pass (see fa_bwd.hip for the gradient formulas): one
-// workgroup per 128-key block, 32 keys per wave with K and V in registers; streams 64-query
-// tiles of Q, dO and the row terms from HBM/L2 straight into LDS, double buffered.
+// workgroup per 128-key block; streams 64-query tiles of Q, dO and the row terms from HBM/L2
+// straight into LDS, double buffered.
 // S = Q K^T and dP = dO V^T are computed with lanes <-> keys, so P and dS leave the
 // accumulators in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS.
 #include "fa_bwd_common.h"
@@ -9,16 +9,24 @@ namespace fa {
 namespace bwd {
 namespace {
 
+// Eight waves, two per SIMD. Wave (kg, qh) = (wave % 4, wave / 4) owns the 32 keys
+// k0 + 32 kg .. and the 32-query half qh of every streamed tile; it holds K of its keys in
+// registers and reads V of the block's 128 keys from LDS (loaded once), which keeps each
+// wave within 256 registers. The two waves of a key group sum their partial dK and dV
+// through LDS at the end.
 template <int D, class T, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int BKV = 32 * kWaves;  // keys per workgroup
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = 8;
+  constexpr int BKV = 128;  // keys per workgroup
   constexpr int DC = D / 16, DB = D / 32;
-  using TL = Tile<D>;
+  using TL = Tile<D, NW>;
 
   __shared__ __attribute__((aligned(1024))) uint8_t Qs0[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t Qs1[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t dOs0[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t dOs1[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vk0[TL::BYTES];  // V rows k0 .. k0+63
+  __shared__ __attribute__((aligned(1024))) uint8_t Vk1[TL::BYTES];  // V rows k0+64 .. k0+127
   __shared__ __attribute__((aligned(256))) float nl0[kTile];  // -LSE log2(e)
   __shared__ __attribute__((aligned(256))) float nl1[kTile];
   __shared__ __attribute__((aligned(256))) float nd0[kTile];  // -D
@@ -27,6 +35,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3, qh = wave >> 2;
   Lanes<D> ln(lane);
   const int nkb = (a.N + BKV - 1) / BKV;
   int kb, h, bs;
@@ -48,17 +57,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const auto rnl = make_rsrc(a.neg_lse2 + si.stat, (uint32_t)L * 4);
   const auto rnd = make_rsrc(a.neg_delta + si.stat, (uint32_t)L * 4);
 
-  const int wk0 = k0 + wave * 32;  // this wave's keys: wk0 .. wk0+31
-  const int key = wk0 + l32;       // the key this lane's accumulators belong to
+  const int wk0 = k0 + kg * 32;  // this wave's keys: wk0 .. wk0+31
+  const int key = wk0 + l32;     // the key this lane's accumulators belong to
 
-  // K and V of this wave's keys: B operands of S = Q K^T and dP = dO V^T. A negative
-  // softmax scale is folded into K's sign (the gradient below then uses the signed scale).
-  u32x4 kreg[DC], vreg[DC];
+  // K of this wave's keys: B operand of S = Q K^T (negative scale folded into its sign)
+  u32x4 kreg[DC];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
+  for (int dc = 0; dc < DC; ++dc)
     kreg[dc] = buf_load16(rk, (uint32_t)key * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
-    vreg[dc] = buf_load16(rv, (uint32_t)key * rstride + (16 * dc + 8 * g) * 2);
-  }
+  // V of the block's keys into LDS (B operand of dP = dO V^T, row fragments)
+  TL::load(rv, Vk0, k0, rstride, wave, lane);
+  TL::load(rv, Vk1, k0 + kTile, rstride, wave, lane);
+  const uint8_t* vk = kg < 2 ? Vk0 : Vk1;
+  const int vrow0 = (kg & 1) * 32;
 
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -87,58 +98,53 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const float* nd = B ? nd1 : nd0;
     if (qt + 1 < qt_end) load_tile(qt + 1, B ? Qs0 : Qs1, B ? dOs0 : dOs1, B ? nl0 : nl1,
                                    B ? nd0 : nd1);
-    const int q0 = qt * kTile;
-    const bool active = !CAUSAL || q0 + kTile - 1 >= wk0;
+    const int q0 = qt * kTile + qh * 32;  // this wave's 32 queries: q0 .. q0+31
+    const bool active = !CAUSAL || q0 + 31 >= wk0;
     if (active) {
-      const bool diag = CAUSAL && q0 < wk0 + 31;
-      // the two 32-query halves of the tile, one after the other
+      ln.refresh();
+      // S (queries x keys) and dP - D (the accumulator starts at -D of each query)
+      f32x16 s = f32x16{}, dp;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        ln.refresh();
-        // S (queries x keys) and dP - D (the accumulator starts at -D of each query)
-        f32x16 s = f32x16{}, dp;
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&nd[qh * 32 + 8 * a4 + 4 * g]);
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&nd[qb * 32 + 8 * a4 + 4 * g]);
+        for (int j = 0; j < 4; ++j) dp[4 * a4 + j] = d4[j];
+      }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) dp[4 * a4 + j] = d4[j];
-        }
+      for (int dc = 0; dc < DC; ++dc) {
+        s = mfma32<T>(ln.row_frag(qs, qh * 32, dc), kreg[dc], s);
+        dp = mfma32<T>(ln.row_frag(dos, qh * 32, dc), ln.row_frag(vk, vrow0, dc), dp);
+      }
+      float p[16];
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          s = mfma32<T>(ln.row_frag(qs, qb * 32, dc), kreg[dc], s);
-          dp = mfma32<T>(ln.row_frag(dos, qb * 32, dc), vreg[dc], dp);
-        }
-        float p[16];
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&nl[qh * 32 + 8 * a4 + 4 * g]);
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&nl[qb * 32 + 8 * a4 + 4 * g]);
+        for (int j = 0; j < 4; ++j) p[4 * a4 + j] = exp2f_hw(fmaf(s[4 * a4 + j], c2, l4[j]));
+      }
+      if (CAUSAL && q0 < wk0 + 31) {
+        __builtin_amdgcn_sched_barrier(0);  // keep the mask a branch (diagonal tiles only)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p[4 * a4 + j] = exp2f_hw(fmaf(s[4 * a4 + j], c2, l4[j]));
-        }
-        if (diag) {
-          __builtin_amdgcn_sched_barrier(0);  // keep the mask a branch (diagonal tiles only)
+        for (int r = 0; r < 16; ++r)
+          if (key > q0 + 8 * (r >> 2) + 4 * g + (r & 3)) p[r] = 0.f;
+      }
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key > q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) p[r] = 0.f;
-        }
+      for (int hh = 0; hh < 2; ++hh) {
+        float ds[8];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          float ds[8];
+        for (int j = 0; j < 8; ++j) ds[j] = p[8 * hh + j] * dp[8 * hh + j];
+        const u32x4 pf = {pack2<T>(p[8 * hh + 0], p[8 * hh + 1]),
+                          pack2<T>(p[8 * hh + 2], p[8 * hh + 3]),
+                          pack2<T>(p[8 * hh + 4], p[8 * hh + 5]),
+                          pack2<T>(p[8 * hh + 6], p[8 * hh + 7])};
+        const u32x4 sf = {pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]),
+                          pack2<T>(ds[4], ds[5]), pack2<T>(ds[6], ds[7])};
+        // dV^T += dO^T P and dK^T += Q^T dS over the 16-query chunk 2 qh + hh of the tile
+        const int kc = 2 * qh + hh;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) ds[j] = p[8 * hh + j] * dp[8 * hh + j];
-          const u32x4 pf = {pack2<T>(p[8 * hh + 0], p[8 * hh + 1]),
-                            pack2<T>(p[8 * hh + 2], p[8 * hh + 3]),
-                            pack2<T>(p[8 * hh + 4], p[8 * hh + 5]),
-                            pack2<T>(p[8 * hh + 6], p[8 * hh + 7])};
-          const u32x4 sf = {pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]),
-                            pack2<T>(ds[4], ds[5]), pack2<T>(ds[6], ds[7])};
-          // dV^T += dO^T P and dK^T += Q^T dS over the 16-query chunk 2 qb + hh
-          const int kc = 2 * qb + hh;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            dvacc[db] = mfma32<T>(ln.tr_frag(dos, kc * 16, db), pf, dvacc[db]);
-            dkacc[db] = mfma32<T>(ln.tr_frag(qs, kc * 16, db), sf, dkacc[db]);
-          }
+        for (int db = 0; db < DB; ++db) {
+          dvacc[db] = mfma32<T>(ln.tr_frag(dos, kc * 16, db), pf, dvacc[db]);
+          dkacc[db] = mfma32<T>(ln.tr_frag(qs, kc * 16, db), sf, dkacc[db]);
         }
       }
     }
@@ -153,6 +159,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     step(std::integral_constant<int, 0>{}, qt);
     if (qt + 1 < qt_end) step(std::integral_constant<int, 1>{}, qt + 1);
   }
+
+  // sum the two query halves' partial gradients of each key group through LDS (the tile
+  // buffers are free now: one per key group, DB*16 floats per lane)
+  uint8_t* red = kg == 0 ? Qs0 : (kg == 1 ? Qs1 : (kg == 2 ? dOs0 : dOs1));
+  auto reduce = [&](f32x16 (&acc)[DB]) {
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(red + ((db * 4 + q4) * 64 + lane) * 16) =
+              f32x4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2],
+                    acc[db][4 * q4 + 3]};
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(red + ((db * 4 + q4) * 64 + lane) * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[db][4 * q4 + j] += o[j];
+        }
+    }
+    __syncthreads();
+  };
+  reduce(dvacc);
+  reduce(dkacc);
+  if (qh != 0) return;
 
   // dK = scale * sum dS q (signed scale), dV = sum P dO
   const float ks = a.scale;
@@ -170,12 +206,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
-
 template <int D, class T, bool CAUSAL, bool VARLEN>
 hipError_t launch_t(const BwdArgs& a, hipStream_t st) {
   const long nblk = (long)((a.N + 127) / 128) * a.H * a.B;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(kThreads), 0,
-                     st, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(512),
+                     0, st, a);
   return hipGetLastError();
 }
 
