@@ -31,8 +31,11 @@ CFLAGS = [
 # directly, so its MFMA results are kept in VGPRs (in AGPRs they would be copied back for
 # every tile); the dK/dV kernel keeps the default (its 128 gradient accumulators live in
 # AGPRs).
+# The forward kernel's row max reads MFMA results; without NaN semantics fmaxf needs no
+# canonicalizing instruction per input (NaN inputs still propagate through exp and the sums).
 FILE_FLAGS = {
     "fa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa_fwd.hip": ["-fno-honor-nans"],
 }
 
 

@@ -67,6 +67,27 @@ __device__ __forceinline__ float add_pair<F16>(uint32_t pair, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
 }
 
+// The pair (1, 1) of the element type as packed bits, and acc + pair[0] + pair[1] with the
+// ones passed in (a register instead of a literal in every dot product).
+template <class T>
+__device__ __forceinline__ uint32_t one_pair();
+template <>
+__device__ __forceinline__ uint32_t one_pair<BF16>() { return 0x3f803f80u; }
+template <>
+__device__ __forceinline__ uint32_t one_pair<F16>() { return 0x3c003c00u; }
+template <class T>
+__device__ __forceinline__ float add_pair_r(uint32_t pair, uint32_t ones, float acc);
+template <>
+__device__ __forceinline__ float add_pair_r<BF16>(uint32_t pair, uint32_t ones, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                         __builtin_bit_cast(bf16x2, ones), acc, false);
+}
+template <>
+__device__ __forceinline__ float add_pair_r<F16>(uint32_t pair, uint32_t ones, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, ones),
+                                acc, false);
+}
+
 // 16-bit element -> fp32 (exact).
 template <class T>
 __device__ __forceinline__ float to_f32(uint32_t bits16);

@@ -8,12 +8,17 @@
 // inside the kernel ("FlashAttention 与算子融合", fusion table).
 //
 // Mapping onto CDNA4:
-//  - one workgroup = 4 waves = 128 query rows of one (batch or sequence, head); wave w
-//    owns 32 consecutive rows, held as MFMA B operands in registers for the whole loop.
+//  - one workgroup = 8 waves = 256 query rows of one (batch or sequence, head); each wave
+//    owns 32 rows, held as MFMA B operands in registers for the whole loop.
+//  - ping-pong: the waves form two groups of four (one wave of each group per SIMD). Each
+//    wave alternates an MFMA phase X_t = [O += P(t-1) V(t-1); S(t) = scores of tile t]
+//    and a vector phase Y_t = [online softmax of S(t) -> P(t)], group B one phase behind
+//    group A, with a workgroup barrier between phases; so on every SIMD one wave issues
+//    matrix instructions while the other does the exp/max/convert work.
 //  - key/value tiles of 64 rows go from HBM/L2 straight into LDS (buffer_load ... lds,
-//    bounds-checked so rows past the sequence read as zero), double buffered: the loads
-//    of tile t+1 are issued before tile t is computed. Rows are stored unpadded with an
-//    XOR swizzle of their 16-byte chunks that keeps the operand reads conflict-free.
+//    bounds-checked so rows past the sequence read as zero), double buffered, issued by
+//    group B during its vector phases. Rows are stored unpadded with an XOR swizzle of
+//    their 16-byte chunks that keeps the operand reads conflict-free.
 //  - scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: each lane then
 //    holds 32 scores of ONE query row (the other 32 sit in lane l^32), so row max and row
 //    sum need only per-lane work plus one v_permlane32_swap.
@@ -36,11 +41,8 @@
 namespace fa {
 namespace {
 
-#ifndef FA_FWD_OCC
-#define FA_FWD_OCC 2  // workgroups per CU the register budget is sized for
-#endif
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBK = 64;                   // keys per tile
 constexpr float kRescaleSlack = 8.0f;     // log2 units the reference max may lag behind
@@ -59,27 +61,58 @@ __device__ __forceinline__ int kswz(int r) { return r & (D / 8 - 1); }
 template <int D>
 __device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
+#ifndef FA_FWD_PREFETCH
+#define FA_FWD_PREFETCH 4  // MFMAs of look-ahead for the LDS operand reads of a matrix phase
+#endif
+
+// Instruction order of one matrix phase: NPV MFMAs with two LDS reads each (O += P V), then
+// NS MFMAs with one read each (S = K Q^T). The reads run PD MFMAs ahead of their use, so the
+// LDS latency is covered by the wave's own matrix work (the other wave on the SIMD is in its
+// vector phase and cannot cover it).
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+template <int NPV, int NM, int PD, int M>
+__device__ __forceinline__ void xsched_step() {
+  sched_group<kSchedMfma, 1>();
+  if constexpr (M + PD < NM) sched_group<kSchedDsRead, (M + PD < NPV ? 2 : 1)>();
+}
+template <int NPV, int NS, int PD, int... M>
+__device__ __forceinline__ void xsched(std::integer_sequence<int, M...>) {
+  constexpr int NM = NPV + NS;
+  constexpr int pd = PD < NM ? PD : NM;
+  sched_group<kSchedDsRead, (pd <= NPV ? 2 * pd : 2 * NPV + (pd - NPV))>();
+  (xsched_step<NPV, NM, PD, M>(), ...);
+}
+
 template <int D, class T, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   constexpr int BQ = 32 * kWaves;
   constexpr int ROWB = D * 2;                 // bytes per K/V row in LDS
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int TILEB = kBK * ROWB;           // bytes per tile
   constexpr int RPL = 1024 / ROWB;            // rows per 1 KiB direct load (one per wave)
-  constexpr int LPW = TILEB / 1024 / kWaves;  // direct loads per wave per tile
+  constexpr int LPW = TILEB / 1024 / (kWaves / 2);  // direct loads per group-B wave per tile
   constexpr int DC = D / 16;                  // 16-wide d chunks of Q K^T
   constexpr int DB = D / 32;                  // 32-wide d blocks of the output
 
-  // separate objects per buffer: the compiler can then see that the direct loads into one
-  // buffer do not alias the reads of the other and need not wait for them
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks0[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks1[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs0[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs1[TILEB];
+  // four tile buffers: K at 0 and TILEB, V at 2 TILEB and 3 TILEB. A buffer's parity is bit
+  // log2(TILEB) of its offset, so switching buffers is an XOR of the per-lane offsets.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];
+  uint8_t* const Ks0 = smem;
+  uint8_t* const Ks1 = smem + TILEB;
+  uint8_t* const Vs0 = smem + 2 * TILEB;
+  uint8_t* const Vs1 = smem + 3 * TILEB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // group (0 = A, 1 = B) and this wave's 32-row block: the groups take alternate blocks so
+  // that causal work is balanced between them; waves w and w+4 share a SIMD
+  const int grp = wave >> 2;
+  const int rb = 2 * (wave & 3) + grp;
 
   // ---- work item: (query block, head, batch or sequence)
   const int nqb = (a.N + BQ - 1) / BQ;
@@ -114,7 +147,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
   const auto ro = make_rsrc(a.o + base, nbytes);
   float* lse = a.lse + (VARLEN ? (long)h * a.T + tok0 : ((long)bs * a.H + h) * a.N);
 
-  const int wq0 = q0 + wave * 32;  // first query row of this wave
+  const int wq0 = q0 + rb * 32;  // first query row of this wave
   const int qi = wq0 + l32;        // this lane's query row
   const int kend = CAUSAL ? (L < q0 + BQ ? L : q0 + BQ) : L;
   const int ntiles = (kend + kBK - 1) / kBK;
@@ -128,10 +161,10 @@ __global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
   // ---- direct HBM/L2 -> LDS tile loads: this wave fills LPW 1 KiB blocks of each tile;
   // lane l of a block writes row blk*RPL + l/CPR, physical chunk l%CPR.
   const int lrow = lane / CPR, lpc = lane % CPR;
-  auto tload = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* tile, int t, bool is_k) {
+  auto tload = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* tile, int t, bool is_k) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int blk = wave * LPW + j;
+      const int blk = (wave & 3) * LPW + j;
       const int row = blk * RPL + lrow;
       const int c = lpc ^ (is_k ? kswz<D>(row) : vswz<D>(row));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -140,121 +173,202 @@ __global__ __launch_bounds__(kThreads, FA_FWD_OCC) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  // ---- per-lane LDS byte offsets of the MFMA operand reads
-  // K (A operand of S^T): row kb*32 + l32, logical chunk 2*dc + g
-  const int krow_off = l32 * ROWB;
+  // ---- per-lane LDS byte offsets of the MFMA operand reads, relative to a tile buffer.
+  // The XOR swizzle is folded into one offset per d chunk (K) or d block (V), so every read
+  // is one of these registers plus a constant.
+  // K (A operand of S^T): row kb*32 + l32, logical chunk 2dc + g, stored at (2dc + g) ^ m,
+  // m = l32 % (D/8); bit 0 comes from g alone, so this is 2(dc ^ m/2) + (g ^ m%2).
+  const int km = kswz<D>(l32);
+  int kcur[DC];  // offsets into the K buffer of the current tile (starts at K buffer 0)
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    kcur[dc] = l32 * ROWB + (2 * (dc ^ (km >> 1)) + (g ^ (km & 1))) * 16;
   // V^T (A operand of O^T): tr reads of keys kc*16 + 4g + i/4 (+8), dims db*32 + 16G + 4(i%4)
+  // (i = lane % 16): logical chunk 4db + x, x = 2G + (i%4)/2, stored at (4db + x) ^ vsw =
+  // 4(db ^ vsw/4) + x, at byte 8(i%2) of the chunk.
   const int i16 = lane & 15, G = (lane >> 4) & 1;
   const int vkey = 4 * g + (i16 >> 2);
   const int vsw = vswz<D>(vkey);
-  const int vhalf = 8 * (i16 & 1);
+  int vcur[DB];  // offsets into the V buffer of the previous tile (V buffer 1 before tile 0)
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    vcur[db] = 3 * TILEB + vkey * ROWB + (4 * (db ^ (vsw >> 2)) + 2 * G + ((i16 & 3) >> 1)) * 16 +
+               8 * (i16 & 1);
 
   float mref = kNegInf, lsum = 0.f;
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   const float c2 = a.scale_log2;
+  // the pair (1, 1) of the element type, kept in a register for the row-sum dot products
+  uint32_t ones = one_pair<T>();
+  asm volatile("" : "+v"(ones));
 
-  // one pipeline step on tile t held in buffer B (B = t % 2): issue the direct loads of
-  // tile t+1 into the other buffer, compute tile t, then wait for this wave's loads and
-  // meet the other waves at the barrier.
-  auto step = [&](auto bsel, int t) {
-    constexpr int B = decltype(bsel)::value;
-    const uint8_t* kt = B ? Ks1 : Ks0;
-    const uint8_t* vt = B ? Vs1 : Vs0;
-    if (t + 1 < ntiles) {
-      tload(rk, B ? Ks0 : Ks1, t + 1, true);
-      tload(rv, B ? Vs0 : Vs1, t + 1, false);
-    }
-    const int kt0 = t * kBK;
-    const bool active = !CAUSAL || kt0 <= wq0 + 31;
-    if (active) {
-      // S^T tile: two 32-key blocks
-      f32x16 s[2];
-      s[0] = s[1] = f32x16{};
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int c = (2 * dc + g) ^ kswz<D>(l32);  // row kb*32 + l32 has the same swizzle
-          const u32x4 ka =
-              *reinterpret_cast<const u32x4*>(kt + kb * 32 * ROWB + krow_off + c * 16);
-          s[kb] = mfma32<T>(ka, qreg[dc], s[kb]);
-        }
+  const int nt_w = CAUSAL ? min(ntiles, (wq0 + 31 + kBK) / kBK) : ntiles;  // this wave's tiles
+  f32x16 s[2];
+  u32x4 pf[4];
 
-      const bool masked = kt0 + kBK > L || (CAUSAL && kt0 + kBK - 1 > wq0);
-      if (masked) {
-        // a real branch: keeps the per-element mask out of the unmasked tiles
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= L || (CAUSAL && key > qi)) s[kb][r] = kNegInf;
-          }
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      const float mnew = pair_max(mx) * c2;  // c2 > 0: a fully masked row keeps -inf
-      const bool need = mnew > mref + kRescaleSlack;
-      if (__any(need)) {
-        const float alpha = need ? exp2f_hw(mref - mnew) : 1.0f;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        if (need) mref = mnew;
-      }
-      // masked scores are -inf and c2 > 0, so their exponent is exactly 0
-      const float mu = mref == kNegInf ? 0.f : mref;
-      u32x4 pf[4];
-      float ls = lsum;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * kc + j;
-          p[j] = exp2f_hw(fmaf(s[r >> 4][r & 15], c2, -mu));
-        }
-        // P rounded to the element type; the row sum adds exactly the rounded values
-        pf[kc] = u32x4{pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]),
-                       pack2<T>(p[6], p[7])};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ls = add_pair<T>(pf[kc][e], ls);
-      }
-      lsum = ls;
-
-      // O^T += V^T P^T over four 16-key chunks
+  // Matrix phase X(t) = [O += P(t-1) V(t-1); S(t) = K(t) Q^T]; S^T has lanes <-> query rows.
+  // It ends by moving the buffer offsets on to tile t+1.
+  auto xphase = [&](auto HAS_PV, auto HAS_S) __attribute__((always_inline)) {
+    if constexpr (decltype(HAS_PV)::value) {
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int c = (db * 4 + 2 * G + ((i16 & 3) >> 1)) ^ vsw;
-          const int off = (kc * 16 + vkey) * ROWB + c * 16 + vhalf;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + off));
-          const i16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + off + 8 * ROWB));
+          const uint8_t* src = smem + vcur[db] + kc * 16 * ROWB;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * ROWB));
           const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
           const u32x4 va = {lo2[0], lo2[1], hi2[0], hi2[1]};
           oacc[db] = mfma32<T>(va, pf[kc], oacc[db]);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's tile t+1 loads have landed in LDS
-    __syncthreads();
+    if constexpr (decltype(HAS_S)::value) {
+      s[0] = s[1] = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(smem + kcur[dc] + kb * 32 * ROWB);
+          s[kb] = mfma32<T>(ka, qreg[dc], s[kb]);
+        }
+    }
+    if constexpr (decltype(HAS_PV)::value && decltype(HAS_S)::value)
+      xsched<4 * DB, 2 * DC, FA_FWD_PREFETCH>(std::make_integer_sequence<int, 4 * DB + 2 * DC>{});
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) kcur[dc] ^= TILEB;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vcur[db] ^= TILEB;
   };
 
-  tload(rk, Ks0, 0, true);
-  tload(rv, Vs0, 0, false);
+  // Y_t: online softmax of S(t) -> P(t), rescaling O (which holds P V up to tile t-1)
+  auto yphase = [&](int t) __attribute__((always_inline)) {
+    const int kt0 = t * kBK;
+    const bool masked = kt0 + kBK > L || (CAUSAL && kt0 + kBK - 1 > wq0);
+    if (masked) {
+      // a real branch: keeps the per-element mask out of the unmasked tiles
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool drop = key >= L || (CAUSAL && key > qi);
+          s[kb][r] = drop ? kNegInf : s[kb][r];
+        }
+    }
+    // Row max as a tree of independent maxima: one wave runs this phase alone on its SIMD,
+    // so the dependency depth, not the instruction count, sets the phase length.
+    float m8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x16& x = s[i >> 2];
+      const int r = 4 * (i & 3);
+      m8[i] = fmaxf(fmaxf(x[r], x[r + 1]), fmaxf(x[r + 2], x[r + 3]));
+    }
+    const float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                           fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+    const float mnew = pair_max(mx) * c2;  // c2 > 0: a fully masked row keeps -inf
+    const bool need = mnew > mref + kRescaleSlack;
+    if (__any(need)) {
+      const float alpha = need ? exp2f_hw(mref - mnew) : 1.0f;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      if (need) mref = mnew;
+    }
+    // masked scores are -inf and c2 > 0, so their exponent is exactly 0
+    const float mu = mref == kNegInf ? 0.f : mref;
+    float ls[4];  // four independent partial row sums (one per 16-key chunk)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * kc + j;
+        p[j] = exp2f_hw(fmaf(s[r >> 4][r & 15], c2, -mu));
+      }
+      // P rounded to the element type; the row sum adds exactly the rounded values
+      pf[kc] = u32x4{pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]),
+                     pack2<T>(p[6], p[7])};
+      ls[kc] = kc == 0 ? lsum : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ls[kc] = add_pair_r<T>(pf[kc][e], ones, ls[kc]);
+    }
+    lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  // Group B issues the direct loads at the start of its vector phase Y(t): K(t+2) into
+  // K buffer t % 2 and V(t+1) into V buffer (t+1) % 2, the buffers both groups finished reading at
+  // the previous barrier; they have landed (vmcnt 0 in the issuing waves) by the barrier
+  // that closes the next phase.
+  auto loads = [&](int t) __attribute__((always_inline)) {
+    if (t + 2 < ntiles) tload(rk, (t & 1) ? Ks1 : Ks0, t + 2, true);
+    if (t + 1 < ntiles) tload(rv, (t & 1) ? Vs0 : Vs1, t + 1, false);
+  };
+  using I0 = std::integral_constant<bool, false>;
+  using I1 = std::integral_constant<bool, true>;
+  // workgroup barrier between phases; the scheduling barriers keep each phase's
+  // instructions on their side of it
+  auto phase_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Results a phase hands to the next one are pinned on its side of the barrier: without
+  // this the compiler sinks their computation to the point of use, past the barrier.
+  auto pin_s = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+  };
+  auto pin_p = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) asm volatile("" : "+v"(pf[kc]));
+  };
+  auto finish_x = [&]() __attribute__((always_inline)) {
+    if (grp == 1) __builtin_amdgcn_s_waitcnt(0);
+    phase_barrier();
+  };
+  // X(t) then Y(t), for 1 <= t < nt_w
+  auto step = [&](int t) __attribute__((always_inline)) {
+    xphase(I1{}, I1{});
+    pin_s();
+    finish_x();
+    if (grp == 1) loads(t);
+    yphase(t);
+    pin_p();
+    phase_barrier();
+  };
+
+  // Phase p: group A runs X(p/2) for even p and Y(p/2) for odd p, group B one phase later.
+  // A wave's own tiles end at nt_w; it then passes the remaining barriers idle.
+  if (grp == 1) tload(rk, Ks0, 0, true);
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+  phase_barrier();
+  if (grp == 1) {
+    if (ntiles > 1) tload(rk, Ks1, 1, true);
+    tload(rv, Vs0, 0, false);
+    phase_barrier();
   }
+  xphase(I0{}, I1{});
+  pin_s();
+  finish_x();
+  if (grp == 1) loads(0);
+  yphase(0);
+  pin_p();
+  phase_barrier();
+  int t = 1;
+#pragma unroll 1
+  for (; t < nt_w; ++t) step(t);
+  // t == nt_w: the last P V
+  xphase(I1{}, I0{});
+  finish_x();
+  for (; t < ntiles; ++t) {
+    if (grp == 1) loads(t);
+    phase_barrier();
+    finish_x();
+  }
+  if (grp == 0) phase_barrier();
 
   // ---- epilogue: O = acc / l (rows >= L are dropped by the buffer bounds), LSE
   const float l = pair_sum(lsum);
