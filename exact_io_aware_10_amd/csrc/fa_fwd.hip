@@ -44,7 +44,13 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBK = 64;                   // keys per tile
+#ifndef FA_FWD_BK
+#define FA_FWD_BK 128
+#endif
+constexpr int kBK = FA_FWD_BK;            // keys per tile
+constexpr int kKB = kBK / 32;             // 32-key blocks of S^T per tile
+constexpr int kKC = kBK / 16;             // 16-key chunks of P per tile (one MFMA k-step each)
+static_assert(kBK == 64 || kBK == 128, "tile of 64 or 128 keys");
 constexpr float kRescaleSlack = 8.0f;     // log2 units the reference max may lag behind
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_inff();
@@ -205,15 +211,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   asm volatile("" : "+v"(ones));
 
   const int nt_w = CAUSAL ? min(ntiles, (wq0 + 31 + kBK) / kBK) : ntiles;  // this wave's tiles
-  f32x16 s[2];
-  u32x4 pf[4];
+  f32x16 s[kKB];
+  u32x4 pf[kKC];
 
   // Matrix phase X(t) = [O += P(t-1) V(t-1); S(t) = K(t) Q^T]; S^T has lanes <-> query rows.
   // It ends by moving the buffer offsets on to tile t+1.
   auto xphase = [&](auto HAS_PV, auto HAS_S) __attribute__((always_inline)) {
     if constexpr (decltype(HAS_PV)::value) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
+      for (int kc = 0; kc < kKC; ++kc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const uint8_t* src = smem + vcur[db] + kc * 16 * ROWB;
@@ -225,17 +231,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
         }
     }
     if constexpr (decltype(HAS_S)::value) {
-      s[0] = s[1] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < kKB; ++kb) {
           const u32x4 ka = *reinterpret_cast<const u32x4*>(smem + kcur[dc] + kb * 32 * ROWB);
           s[kb] = mfma32<T>(ka, qreg[dc], s[kb]);
         }
     }
     if constexpr (decltype(HAS_PV)::value && decltype(HAS_S)::value)
-      xsched<4 * DB, 2 * DC, FA_FWD_PREFETCH>(std::make_integer_sequence<int, 4 * DB + 2 * DC>{});
+      xsched<kKC * DB, kKB * DC, FA_FWD_PREFETCH>(
+          std::make_integer_sequence<int, kKC * DB + kKB * DC>{});
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) kcur[dc] ^= TILEB;
 #pragma unroll
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       // a real branch: keeps the per-element mask out of the unmasked tiles
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -260,15 +268,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     }
     // Row max as a tree of independent maxima: one wave runs this phase alone on its SIMD,
     // so the dependency depth, not the instruction count, sets the phase length.
-    float m8[8];
+    float m8[4 * kKB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4 * kKB; ++i) {
       const f32x16& x = s[i >> 2];
       const int r = 4 * (i & 3);
       m8[i] = fmaxf(fmaxf(x[r], x[r + 1]), fmaxf(x[r + 2], x[r + 3]));
     }
-    const float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                           fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+#pragma unroll
+    for (int w = 4 * kKB; w > 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w / 2; ++i) m8[i] = fmaxf(m8[2 * i], m8[2 * i + 1]);
+    const float mx = m8[0];
     const float mnew = pair_max(mx) * c2;  // c2 > 0: a fully masked row keeps -inf
     const bool need = mnew > mref + kRescaleSlack;
     if (__any(need)) {
@@ -280,9 +291,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     }
     // masked scores are -inf and c2 > 0, so their exponent is exactly 0
     const float mu = mref == kNegInf ? 0.f : mref;
-    float ls[4];  // four independent partial row sums (one per 16-key chunk)
+    float ls[kKC];  // independent partial row sums, one per 16-key chunk
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int kc = 0; kc < kKC; ++kc) {
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -296,7 +307,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) ls[kc] = add_pair_r<T>(pf[kc][e], ones, ls[kc]);
     }
-    lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#pragma unroll
+    for (int w = kKC; w > 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w / 2; ++i) ls[i] = ls[2 * i] + ls[2 * i + 1];
+    lsum = ls[0];
   };
 
   // Group B issues the direct loads at the start of its vector phase Y(t): K(t+2) into
@@ -319,11 +334,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // Results a phase hands to the next one are pinned on its side of the barrier: without
   // this the compiler sinks their computation to the point of use, past the barrier.
   auto pin_s = [&]() __attribute__((always_inline)) {
-    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) asm volatile("" : "+v"(s[kb]));
   };
   auto pin_p = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) asm volatile("" : "+v"(pf[kc]));
+    for (int kc = 0; kc < kKC; ++kc) asm volatile("" : "+v"(pf[kc]));
   };
   auto finish_x = [&]() __attribute__((always_inline)) {
     if (grp == 1) __builtin_amdgcn_s_waitcnt(0);
