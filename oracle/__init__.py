@@ -40,10 +40,12 @@ def _load():
         lib.oracle_fwd_blocked.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, D, I, L, L, I, dp, I]
         lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, L, D, I, I]
         lib.oracle_fwd_varlen.argtypes = [dp, dp, dp, dp, dp, ip, L, L, L, L, D, I, I]
+        lib.oracle_fwd_decode.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, D, I, I]
+        lib.oracle_fwd_decode_split.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, D, I, L, I]
         lib.oracle_bwd_varlen.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ip, L, L, L, L,
                                           D, I, I]
         for f in ("oracle_fwd", "oracle_fwd_blocked", "oracle_bwd", "oracle_fwd_varlen",
-                  "oracle_bwd_varlen"):
+                  "oracle_bwd_varlen", "oracle_fwd_decode", "oracle_fwd_decode_split"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -129,6 +131,38 @@ def bwd(q, k, v, o, lse, dout, scale, causal, nthreads=None):
                             nthreads or default_threads())
     _check(rc, "oracle_bwd")
     return dq, dk, dv
+
+
+def fwd_decode(q, k, v, scale, causal, nthreads=None):
+    """Decode shapes. q: fp64 [B, Nq, H, d]; k, v: [B, Nk, H, d]. Query row i stands at
+    position Nk - Nq + i (causal: sees keys j <= Nk - Nq + i). Returns (O [B,Nq,H,d],
+    LSE [B,H,Nq])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    assert k.shape == (B, Nk, H, d) and v.shape == k.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    rc = _load().oracle_fwd_decode(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Nq, Nk, H, d,
+                                   float(scale), int(bool(causal)), nthreads or default_threads())
+    _check(rc, "oracle_fwd_decode")
+    return o, lse
+
+
+def fwd_decode_split(q, k, v, scale, causal, nsplit, nthreads=None):
+    """fwd_decode by key splits combined with the block-merge rule (same results up to
+    rounding)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    assert k.shape == (B, Nk, H, d) and v.shape == k.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    rc = _load().oracle_fwd_decode_split(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Nq, Nk, H, d,
+                                         float(scale), int(bool(causal)), int(nsplit),
+                                         nthreads or default_threads())
+    _check(rc, "oracle_fwd_decode_split")
+    return o, lse
 
 
 def _cu(cu_seqlens):

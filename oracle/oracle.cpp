@@ -29,6 +29,15 @@
 // Varlen: the same with B = 1 and N = total tokens ([T, H, d], lse [H, T]); sequence s
 // occupies tokens [cu[s], cu[s+1]) and is an independent attention problem.
 //
+// Decode shapes (Nq query rows against Nk keys, e.g. the last Nq positions of a sequence
+// whose keys and values are all cached): query row i stands at position Nk - Nq + i; with
+// the causal mask it sees keys j <= Nk - Nq + i (none when that is negative), without it all
+// Nk keys. For Nq = Nk this is the mask above. The split form cuts the keys into contiguous
+// ranges, takes (m, l, O) of each range from the definition restricted to it, and combines
+// them with the block-merge rule ("FlashAttention 与算子融合", section on the two keys of
+// FlashAttention): m = max_s m_s, l = sum_s l_s exp(m_s - m), and the outputs rescaled the
+// same way, O = sum_s O_s l_s exp(m_s - m) / l.
+//
 // Threads only split independent output rows (or heads); every sum is accumulated in
 // natural index order, so results do not depend on the thread count.
 
@@ -234,6 +243,75 @@ const long kRowChunk = 32;
 
 bool bad_sizes(long B, long N, long H, long d) { return B < 0 || N < 0 || H <= 0 || d <= 0; }
 
+// ---------------------------------------------------------------- decode shapes
+// Keys visible to query row i of Nq against Nk keys (see the header).
+long decode_visible_end(long i, long Nq, long Nk, int causal) {
+  if (!causal) return Nk;
+  const long e = Nk - Nq + i + 1;
+  return e < 0 ? 0 : (e > Nk ? Nk : e);
+}
+
+// One (batch, head) of a decode problem.
+struct DecodeSlice {
+  const double* q;  // query row i at q + i * rs
+  const double* k;  // key row j at k + j * rs
+  const double* v;
+  long rs;          // row stride in elements (H * d)
+  long Nq, Nk;
+};
+
+// (m, l, O) of query row i over the visible keys in [j0, j1): the plain definition restricted
+// to those keys, O normalised by l. An empty range gives m = -inf, l = 0, O = 0.
+void decode_partial(const DecodeSlice& s, long d, double scale, int causal, long i, long j0,
+                    long j1, double* o, double& m, double& l) {
+  const long je = std::min(j1, decode_visible_end(i, s.Nq, s.Nk, causal));
+  const double* qi = s.q + i * s.rs;
+  for (long c = 0; c < d; ++c) o[c] = 0.0;
+  m = kNegInf;
+  l = 0.0;
+  if (je <= j0) return;
+  std::vector<double> sc(je - j0);
+  for (long j = j0; j < je; ++j) {
+    sc[j - j0] = scale * dot(qi, s.k + j * s.rs, d);
+    m = std::max(m, sc[j - j0]);
+  }
+  for (long j = j0; j < je; ++j) {
+    const double p = std::exp(sc[j - j0] - m);
+    l += p;
+    const double* vj = s.v + j * s.rs;
+    for (long c = 0; c < d; ++c) o[c] += p * vj[c];
+  }
+  for (long c = 0; c < d; ++c) o[c] /= l;
+}
+
+// Block-merge rule over n partial results (m_s, l_s, O_s), O_s normalised by l_s.
+void merge_partials(long n, long d, const double* ms, const double* ls, const double* os,
+                    double* o, double& lse) {
+  double m = kNegInf;
+  for (long t = 0; t < n; ++t) m = std::max(m, ms[t]);
+  for (long c = 0; c < d; ++c) o[c] = 0.0;
+  if (m == kNegInf) {  // no visible key in any part
+    lse = kNegInf;
+    return;
+  }
+  double l = 0.0;
+  for (long t = 0; t < n; ++t) {
+    if (ls[t] == 0.0) continue;
+    const double w = ls[t] * std::exp(ms[t] - m);
+    l += w;
+    for (long c = 0; c < d; ++c) o[c] += w * os[t * d + c];
+  }
+  for (long c = 0; c < d; ++c) o[c] /= l;
+  lse = m + std::log(l);
+}
+
+DecodeSlice decode_slice(const double* q, const double* k, const double* v, long Nq, long Nk,
+                         long H, long d, long idx) {
+  const long b = idx / H, h = idx % H;
+  return DecodeSlice{q + (b * Nq * H + h) * d, k + (b * Nk * H + h) * d,
+                     v + (b * Nk * H + h) * d, H * d, Nq, Nk};
+}
+
 // Slices of a dense [B, N, H, d] problem: slice index = b * H + h.
 Slice dense_slice(const double* q, const double* k, const double* v, double* o, double* lse,
                   long N, long H, long d, long idx) {
@@ -347,6 +425,45 @@ int oracle_bwd_varlen(const double* q, const double* k, const double* v, const d
                 dout + off, dq + off, dk + off, dv + off};
     bwd_dq_rows(g, d, scale, causal, 0, L);
     bwd_dkdv_rows(g, d, scale, causal, 0, L);
+  });
+  return 0;
+}
+
+// Decode shapes: q, o [B, Nq, H, d]; k, v [B, Nk, H, d]; lse [B, H, Nq]. Plain definition
+// with the decode visibility rule. Returns 0, or -1 on bad sizes.
+int oracle_fwd_decode(const double* q, const double* k, const double* v, double* o,
+                      double* lse, long B, long Nq, long Nk, long H, long d, double scale,
+                      int causal, int nthreads) {
+  if (B < 1 || Nq < 1 || Nk < 1 || H < 1 || d < 1) return -1;
+  parallel_for(B * H * Nq, nthreads, [&](long it) {
+    const long idx = it / Nq, i = it % Nq;
+    const DecodeSlice s = decode_slice(q, k, v, Nq, Nk, H, d, idx);
+    double* oi = o + ((idx / H) * Nq * H + i * H + idx % H) * d;
+    double m, l;
+    decode_partial(s, d, scale, causal, i, 0, Nk, oi, m, l);
+    lse[idx * Nq + i] = l > 0.0 ? m + std::log(l) : kNegInf;
+  });
+  return 0;
+}
+
+// Split form: the keys cut into nsplit contiguous ranges of ceil(Nk / nsplit) (trailing
+// ranges may be empty), each range's (m, l, O) from the definition, combined by the
+// block-merge rule. Same layouts as oracle_fwd_decode.
+int oracle_fwd_decode_split(const double* q, const double* k, const double* v, double* o,
+                            double* lse, long B, long Nq, long Nk, long H, long d, double scale,
+                            int causal, long nsplit, int nthreads) {
+  if (B < 1 || Nq < 1 || Nk < 1 || H < 1 || d < 1 || nsplit < 1) return -1;
+  const long span = (Nk + nsplit - 1) / nsplit;
+  parallel_for(B * H * Nq, nthreads, [&](long it) {
+    const long idx = it / Nq, i = it % Nq;
+    const DecodeSlice s = decode_slice(q, k, v, Nq, Nk, H, d, idx);
+    std::vector<double> ms(nsplit), ls(nsplit), os(nsplit * d);
+    for (long t = 0; t < nsplit; ++t) {
+      const long j0 = std::min(t * span, Nk), j1 = std::min(j0 + span, Nk);
+      decode_partial(s, d, scale, causal, i, j0, j1, &os[t * d], ms[t], ls[t]);
+    }
+    double* oi = o + ((idx / H) * Nq * H + i * H + idx % H) * d;
+    merge_partials(nsplit, d, ms.data(), ls.data(), os.data(), oi, lse[idx * Nq + i]);
   });
   return 0;
 }

@@ -35,6 +35,13 @@ MUTANTS = {
                         "for (long i = causal ? j + 1 : 0; i < s.L; ++i) {"),
     "varlen_lse_offset": ("lse + h * T + cu[s], H * d, 1, L};\n    fwd_rows",
                           "lse + h * T, H * d, 1, L};\n    fwd_rows"),
+    "decode_causal_off_by_one": ("const long e = Nk - Nq + i + 1;", "const long e = Nk - Nq + i;"),
+    "decode_top_left_mask": ("const long e = Nk - Nq + i + 1;", "const long e = i + 1;"),
+    "merge_weight_sign": ("const double w = ls[t] * std::exp(ms[t] - m);",
+                          "const double w = ls[t] * std::exp(m - ms[t]);"),
+    "merge_drops_l": ("const double w = ls[t] * std::exp(ms[t] - m);",
+                      "const double w = std::exp(ms[t] - m);"),
+    "merge_lse_drops_max": ("lse = m + std::log(l);", "lse = std::log(l);"),
 }
 
 

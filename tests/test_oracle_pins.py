@@ -323,3 +323,105 @@ def test_varlen_length_draw():
         lens = inputs.varlen_lengths(131072, 64, 16384, seed)
         assert sum(lens) == 131072
         assert all(64 <= n <= 16384 for n in lens[:-1]) and 1 <= lens[-1] <= 16384
+
+
+# ---------------------------------------------------------------- decode shapes (Nq != Nk)
+
+@pytest.mark.parametrize("nsplit", [None, 1, 2, 3, 4])
+def test_decode_narration_example(nsplit):
+    # The narration's row as one query against four cached keys: the split form with key
+    # blocks of two is exactly the two-block walk-through (after block two the numerator and
+    # denominator relative to the running maximum 4 are 72.5 and 2.5).
+    g = _golden("narration_online_softmax_example.json")
+    scores = [math.log(1), math.log(2), math.log(4), math.log(3)]
+    q, k, v = _one_row_problem(scores, g["values"])
+    q = q[:, :1]
+    if nsplit is None:
+        o, lse = oracle.fwd_decode(q, k, v, 1.0, False)
+    else:
+        o, lse = oracle.fwd_decode_split(q, k, v, 1.0, False, nsplit)
+    assert o[0, 0, 0, 0] == pytest.approx(g["output"], abs=1e-12)
+    last = g["after_block"][-1]
+    assert o[0, 0, 0, 0] == pytest.approx(last["numerator"] / last["denominator"], abs=1e-12)
+    assert lse[0, 0, 0] == pytest.approx(
+        math.log(last["block_max_exp"] * last["denominator"]), abs=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(1, 7), (3, 7), (7, 7), (9, 5)])
+@pytest.mark.parametrize("nsplit", [None, 3])
+def test_decode_visible_counts(causal, nq, nk, nsplit):
+    # q = 0 makes every visible key weigh the same; v_j = e_j then reads off which keys row i
+    # saw: O_i = (1/n_i) on the first n_i coordinates, LSE_i = ln n_i. Query row i stands at
+    # position nk - nq + i, so with the mask it sees n_i = clamp(nk - nq + i + 1, 0, nk) keys.
+    d = max(nk, 2)
+    q = np.zeros((1, nq, 1, d))
+    k = _rand((1, nk, 1, d), 5)
+    v = np.zeros((1, nk, 1, d))
+    for j in range(nk):
+        v[0, j, 0, j] = 1.0
+    if nsplit is None:
+        o, lse = oracle.fwd_decode(q, k, v, 0.7, causal)
+    else:
+        o, lse = oracle.fwd_decode_split(q, k, v, 0.7, causal, nsplit)
+    for i in range(nq):
+        n = min(max(nk - nq + i + 1, 0), nk) if causal else nk
+        want = np.zeros(d)
+        want[:n] = 1.0 / n if n else 0.0
+        np.testing.assert_allclose(o[0, i, 0], want, atol=1e-14)
+        if n:
+            assert lse[0, 0, i] == pytest.approx(math.log(n), abs=1e-13)
+        else:
+            assert lse[0, 0, i] == -math.inf
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_square_is_the_plain_forward(causal):
+    # with as many queries as keys the decode rule is the ordinary (causal) attention
+    q, k, v = (_rand((2, 13, 3, 8), s) for s in (20, 21, 22))
+    o1, l1 = oracle.fwd(q, k, v, 0.4, causal)
+    o2, l2 = oracle.fwd_decode(q, k, v, 0.4, causal)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-13)
+
+
+def test_decode_constant_values():
+    q = _rand((2, 3, 2, 6), 30) * 4
+    k = _rand((2, 19, 2, 6), 31) * 4
+    v = np.broadcast_to(np.arange(6.0) - 2.5, (2, 19, 2, 6)).copy()
+    for causal in (False, True):
+        for nsplit in (1, 4, 25):
+            o, _ = oracle.fwd_decode_split(q, k, v, 0.9, causal, nsplit)
+            np.testing.assert_allclose(o, np.broadcast_to(np.arange(6.0) - 2.5, o.shape),
+                                       rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_split_equals_unsplit(causal):
+    # the block-merge rule reproduces the one-shot softmax for any cut of the keys,
+    # including cuts that leave trailing ranges empty
+    q = _rand((2, 5, 3, 16), 40) * 2
+    k = _rand((2, 37, 3, 16), 41) * 2
+    v = _rand((2, 37, 3, 16), 42)
+    o, lse = oracle.fwd_decode(q, k, v, 0.6, causal)
+    for nsplit in (1, 2, 3, 7, 36, 37, 50):
+        o2, l2 = oracle.fwd_decode_split(q, k, v, 0.6, causal, nsplit)
+        np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l2, lse, rtol=0, atol=1e-12)
+
+
+def test_decode_shift_invariance_and_large_scores():
+    # adding c to every score of a row leaves O unchanged and moves LSE by c; scores near
+    # 1000 do not overflow
+    q = _rand((1, 4, 1, 8), 50)
+    k = _rand((1, 23, 1, 8), 51)
+    v = _rand((1, 23, 1, 8), 52)
+    c = 1000.0
+    q2 = np.concatenate([q, np.ones((1, 4, 1, 1))], axis=-1)
+    k2 = np.concatenate([k, np.full((1, 23, 1, 1), c)], axis=-1)
+    v2 = np.concatenate([v, np.zeros((1, 23, 1, 1))], axis=-1)
+    for causal in (False, True):
+        o, lse = oracle.fwd_decode_split(q, k, v, 1.0, causal, 4)
+        o2, lse2 = oracle.fwd_decode_split(q2, k2, v2, 1.0, causal, 4)
+        np.testing.assert_allclose(o2[..., :8], o, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(lse2, lse + c, rtol=0, atol=1e-9)
