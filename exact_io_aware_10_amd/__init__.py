@@ -7,6 +7,7 @@ current HIP stream. There is no fallback: if the library is missing the calls ra
     o, lse = fa_fwd(q, k, v, causal=False, softmax_scale=None)
     dq, dk, dv = fa_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None)
     o, lse = fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, softmax_scale=None)
+    o, lse = fa_fwd_splitkv(q, k, v, causal=False, softmax_scale=None, num_splits=0)
 
 q, k, v, o, dout: [B, N, H, d] (packed: [T, H, d]) contiguous bf16 or fp16 CUDA tensors;
 lse: fp32 [B, H, N] (packed: [H, T]); d in {64, 128}; softmax_scale defaults to 1/sqrt(d).
@@ -16,7 +17,7 @@ import math
 import os
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen",
-           "fa_bwd_varlen",
+           "fa_bwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
            "fa_bwd_workspace_size", "fa_status_string", "FAError", "library_path",
            "load_library"]
 
@@ -58,6 +59,10 @@ def load_library():
     lib.fa_fwd_varlen.restype = i
     lib.fa_bwd_varlen.argtypes = [vp] * 11 + [i, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_varlen.restype = i
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_splitkv_workspace_size.restype = s
+    lib.fa_fwd_splitkv.argtypes = [vp] * 6 + [i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_splitkv.restype = i
     _lib = lib
     return lib
 
@@ -230,3 +235,37 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, causal=False,
     if rc != FA_OK:
         raise FAError("fa_bwd_varlen", rc)
     return dq, dk, dv
+
+
+def fa_fwd_splitkv_workspace_size(B: int, Nq: int, Nk: int, H: int, d: int,
+                                  num_splits: int = 0) -> int:
+    return int(load_library().fa_fwd_splitkv_workspace_size(B, Nq, Nk, H, d, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, causal=False, softmax_scale=None, num_splits=0, workspace=None):
+    """Split-KV forward for decode shapes. q: [B, Nq, H, d]; k, v: [B, Nk, H, d] (same
+    dtype, contiguous). Query row i stands at position Nk - Nq + i (causal: it sees keys up
+    to that position). Returns (o [B,Nq,H,d], lse fp32 [B,H,Nq])."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Nq, H, d] and k, v [B, Nk, H, d]")
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    _check_tensor("q", q, q.shape, q.dtype, q.device)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, Nk, H, d), q.dtype, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    nbytes = fa_fwd_splitkv_workspace_size(B, Nq, Nk, H, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr(), workspace.data_ptr(), B, Nq, Nk, H, d,
+                            _dtype_code(q), _scale(softmax_scale, d), int(bool(causal)),
+                            int(num_splits), _stream(q.device))
+    if rc != FA_OK:
+        raise FAError("fa_fwd_splitkv", rc)
+    return o, lse

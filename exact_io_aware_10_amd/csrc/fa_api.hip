@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_decode.h"
 #include "fa_internal.h"
 
 #define FA_EXPORT extern "C" __attribute__((visibility("default")))
@@ -201,4 +202,60 @@ FA_EXPORT fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, c
   a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
   return to_status(fa::launch_bwd(a, d, dtype == FA_BF16, causal != 0, true, fa::kBwdAll,
                                   stream));
+}
+
+namespace {
+
+constexpr int kMaxSplits = 4096;
+
+// Valid split-KV sizes: 0 when the request is fine, else the status to return.
+fa_status splitkv_sizes(long B, long Nq, long Nk, long H, int d, int num_splits) {
+  if (B < 0 || Nq < 0 || H < 0 || Nk < 1 || num_splits < 0 || num_splits > kMaxSplits)
+    return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((Nk + 256) * H * d >= kMaxSliceElems || (Nq + 256) * H * d >= kMaxSliceElems)
+    return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+}  // namespace
+
+FA_EXPORT size_t fa_fwd_splitkv_workspace_size(int B, int Nq, int Nk, int H, int d,
+                                               int num_splits) {
+  if (splitkv_sizes(B, Nq, Nk, H, d, num_splits) != FA_OK) return 0;
+  const long S = fa::decode_splits(B, Nq, Nk, H, d, num_splits);
+  const long rows = (long)B * H * S * Nq;
+  // partial outputs (rows x d), then the reference maxima and the sums (rows each)
+  return (size_t)rows * (d + 2) * 4;
+}
+
+FA_EXPORT fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, void* workspace, int B, int Nq, int Nk, int H,
+                                   int d, fa_dtype dtype, float softmax_scale, int causal,
+                                   int num_splits, hipStream_t stream) {
+  fa_status st = splitkv_sizes(B, Nq, Nk, H, d, num_splits);
+  if (st != FA_OK) return st;
+  if (!dtype_ok(dtype) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
+  if ((long)B * Nq * H == 0) return FA_OK;
+  if (!tensors_ok({q, k, v, o, workspace}) || lse == nullptr || ((uintptr_t)lse & 3u))
+    return FA_ERR_INVALID_ARG;
+  fa::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.B = B;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.H = H;
+  a.S = fa::decode_splits(B, Nq, Nk, H, d, num_splits);
+  a.span = fa::decode_span(Nk, a.S);
+  const long rows = (long)B * H * a.S * Nq;
+  a.opart = static_cast<float*>(workspace);
+  a.mpart = a.opart + rows * d;
+  a.lpart = a.mpart + rows;
+  a.scale_log2 = exp_scale(softmax_scale);
+  a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
+  return to_status(fa::launch_decode(a, d, dtype == FA_BF16, causal != 0, stream));
 }

@@ -1,0 +1,350 @@
+// Split-KV forward for decode shapes: a few query rows (Nq, e.g. the newest token of each
+// sequence) against a long cached key/value sequence (Nk). The narration script ("FlashAttention
+// 短片讲解稿", segment 适用范围与关键结论) notes that token-by-token decoding has a different shape
+// from training and prefill; here the work is one pass over K and V, bound by HBM bandwidth,
+// so it is spread over many independent key ranges, each reduced to a partial (O, m, l) by
+// the online softmax, and the partials are combined with the block-merge rule of
+// "FlashAttention 与算子融合" (section on the two keys of FlashAttention):
+//   m = max_s m_s,  l = sum_s l_s exp(m_s - m),  O = sum_s O_s exp(m_s - m) / l.
+//
+// Query row i stands at position Nk - Nq + i of the sequence; the causal mask hides keys
+// after it (for Nq = Nk this is the ordinary causal mask).
+//
+// Kernel 1 (decode_kernel): a workgroup is four independent waves, one key range each, over
+// one block of 32 query rows of one (b, h). A wave holds the Q rows as MFMA B operands and
+// streams its range in 32-key tiles of K and V from HBM straight into its own part of LDS
+// (buffer_load_dwordx4 ... lds, double buffered, issued from inline assembly so that the
+// compiler does not turn its conservative aliasing waits into a wait for the next tile; the
+// wave waits for each tile itself). S^T = K Q^T and O^T += V^T P^T on MFMA as in the forward
+// (the matrix cores have ample headroom at these shapes: the bound is the K/V stream).
+// Tiles use the dual chunk swizzle of the backward kernels, which keeps both the row-fragment
+// reads of K and the transposed reads of V conflict-free.
+// Kernel 2 (combine_kernel): one wave per output row merges the S partials and writes O and
+// LSE.
+#include "fa_bwd_common.h"
+#include "fa_decode.h"
+
+namespace fa {
+namespace dec {
+namespace {
+
+using bwd::Lanes;
+using bwd::swz;
+
+constexpr int kTK = 32;  // keys per tile
+// Independent waves (key ranges) per workgroup and tile buffers per wave: a wave keeps
+// kBufs - 1 tiles in flight while it works on one, within 128 KiB of LDS per workgroup.
+template <int D>
+struct Cfg {
+  static constexpr int kWaves = D == 128 ? 2 : 4;
+  static constexpr int kBufs = 4;
+};
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag behind
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// 16 bytes per lane from a buffer into LDS: lane l writes lds_addr + OFF + 16 l with the
+// bytes at voff + OFF (zeros past the buffer's size). lds_addr is wave-uniform (M0).
+template <int OFF>
+__device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff) {
+  static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen offset:%3 lds"
+               :
+               : "{m0}"(lds_addr), "v"(voff), "s"(rs), "i"(OFF)
+               : "memory");
+}
+// Wait until at most N vector-memory operations of this wave are outstanding. Written in
+// assembly with a memory clobber so that no LDS read moves above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// acc + pair[0] + pair[1] for a packed pair of the element type, with the pair (1, 1) held in
+// a register. The pair is taken by value: a bit cast applied directly to a vector element
+// expression compiled to a cast of element 0.
+template <class T>
+__device__ __forceinline__ float add_pair_ones(uint32_t pair, uint32_t ones, float acc) {
+  if constexpr (std::is_same_v<T, BF16>)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                           __builtin_bit_cast(bf16x2, ones), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair),
+                                  __builtin_bit_cast(f16x2, ones), acc, false);
+}
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, nbytes, 0x00020000u};
+}
+
+template <int D, class T, bool CAUSAL>
+__global__ __launch_bounds__(64 * Cfg<D>::kWaves, 1) void decode_kernel(DecodeArgs a) {
+  constexpr int kWaves = Cfg<D>::kWaves, kBufs = Cfg<D>::kBufs;
+  constexpr int ROWB = D * 2;          // bytes per K/V row
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int TB = kTK * ROWB;       // bytes per tile
+  constexpr int RPL = 1024 / ROWB;     // rows per 1 KiB load
+  constexpr int LPT = TB / 1024;       // loads per tile and tensor
+  constexpr int DC = D / 16, DB = D / 32;
+  static_assert(LPT == 4 || LPT == 8, "tile of 4 or 8 KiB");
+
+  // per wave: kBufs buffers of a K tile and a V tile
+  constexpr int WAVEB = kBufs * 2 * TB;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * WAVEB];
+
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nqb = (a.Nq + 31) / 32;
+  const int G = (a.S + kWaves - 1) / kWaves;
+  uint32_t w = blockIdx.x;
+  const int gs = w % G;
+  w /= G;
+  const int qb = w % nqb;
+  w /= nqb;
+  const int h = w % a.H;
+  const int b = w / a.H;
+  const int s = gs * kWaves + wave;  // this wave's key range
+  if (s >= a.S) return;
+  const int j0 = min(s * a.span, a.Nk);
+  const int j1 = min(j0 + a.span, a.Nk);
+  const int ntile = (j1 - j0 + kTK - 1) / kTK;
+
+  const uint32_t rstride = (uint32_t)a.H * D * 2;
+  const auto rq = make_rsrc(a.q + ((long)b * a.Nq * a.H + h) * D,
+                            (uint32_t)(a.Nq - 1) * rstride + D * 2);
+  const long kvbase = ((long)b * a.Nk * a.H + h) * D;
+  const uint32_t kvbytes = (uint32_t)(a.Nk - 1) * rstride + D * 2;
+  const u32x4 rk = rsrc_words(a.k + kvbase, kvbytes);
+  const u32x4 rv = rsrc_words(a.v + kvbase, kvbytes);
+
+  const int q0 = qb * 32;
+  const int qi = q0 + l32;  // this lane's query row
+  u32x4 qreg[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    qreg[dc] = buf_load16(rq, (uint32_t)qi * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
+
+  // tile loads: block j (1 KiB) holds rows j*RPL + lane/CPR, physical chunk lane%CPR; one M0
+  // per four blocks, the instruction offset selects the block within them
+  const uint32_t mine = (uint32_t)(uintptr_t)(bwd::lds_void*)smem + wave * WAVEB;
+  const int lrow = lane / CPR, lpc = lane % CPR;
+  uint32_t vo[LPT];  // per-lane byte offset of block j relative to the tile's first row
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int row = j * RPL + lrow;
+    vo[j] = (uint32_t)row * rstride + (uint32_t)((lpc ^ swz<D>(row)) * 16) - (j & 3) * 1024;
+  }
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(j0 + t * kTK) * rstride;
+    const uint32_t lk = __builtin_amdgcn_readfirstlane(mine + (t % kBufs) * 2 * TB);
+    const uint32_t lv = lk + TB;
+    dma16<0>(rk, lk, base + vo[0]);
+    dma16<1024>(rk, lk, base + vo[1]);
+    dma16<2048>(rk, lk, base + vo[2]);
+    dma16<3072>(rk, lk, base + vo[3]);
+    if constexpr (LPT == 8) {
+      dma16<0>(rk, lk + 4096, base + vo[4]);
+      dma16<1024>(rk, lk + 4096, base + vo[5]);
+      dma16<2048>(rk, lk + 4096, base + vo[6]);
+      dma16<3072>(rk, lk + 4096, base + vo[7]);
+    }
+    dma16<0>(rv, lv, base + vo[0]);
+    dma16<1024>(rv, lv, base + vo[1]);
+    dma16<2048>(rv, lv, base + vo[2]);
+    dma16<3072>(rv, lv, base + vo[3]);
+    if constexpr (LPT == 8) {
+      dma16<0>(rv, lv + 4096, base + vo[4]);
+      dma16<1024>(rv, lv + 4096, base + vo[5]);
+      dma16<2048>(rv, lv + 4096, base + vo[6]);
+      dma16<3072>(rv, lv + 4096, base + vo[7]);
+    }
+  };
+
+  const Lanes<D> ln(lane);
+  constexpr bool kBf16 = std::is_same_v<T, BF16>;
+  const uint32_t one2 = kBf16 ? 0x3f803f80u : 0x3c003c00u;
+  uint32_t ones = one2;
+  asm volatile("" : "+v"(ones));
+  const float c2 = a.scale_log2;
+  const int qpos = a.Nk - a.Nq + qi;  // position of this lane's query in the sequence
+
+  float mref = kNegInf, lsum = 0.f;
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+
+  // tiles 0 .. kBufs-2 in flight before the loop; iteration t issues tile t + kBufs - 1 and
+  // waits for tile t, leaving the later ones in flight (each tile is 2 * LPT loads)
+#pragma unroll
+  for (int u = 0; u < kBufs - 1; ++u)
+    if (u < ntile) load_tile(u);
+#pragma unroll 1
+  for (int t = 0; t < ntile; ++t) {
+    if (t + kBufs - 1 < ntile) load_tile(t + kBufs - 1);
+    const int later = min(ntile - 1 - t, kBufs - 1);  // tiles issued after tile t
+    if (later >= 3)
+      wait_vmcnt<3 * 2 * LPT>();
+    else if (later == 2)
+      wait_vmcnt<2 * 2 * LPT>();
+    else if (later == 1)
+      wait_vmcnt<2 * LPT>();
+    else
+      wait_vmcnt<0>();
+    const uint8_t* kt = smem + wave * WAVEB + (t % kBufs) * 2 * TB;
+    const uint8_t* vt = kt + TB;
+    // S^T = K Q^T: lane (l32, g) holds the scores of query qi for keys 8(r/4) + 4g + r%4
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) sc = mfma32<T>(ln.row_frag(kt, 0, dc), qreg[dc], sc);
+    const int kt0 = j0 + t * kTK;
+    const bool masked = kt0 + kTK > j1 || (CAUSAL && kt0 + kTK - 1 > a.Nk - a.Nq + q0);
+    if (masked) {
+      __builtin_amdgcn_sched_barrier(0);  // a real branch: tail and diagonal tiles only
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool drop = key >= j1 || (CAUSAL && key > qpos);
+        sc[r] = drop ? kNegInf : sc[r];
+      }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    const float mnew = pair_max(mx) * c2;  // c2 > 0: a row with no visible key keeps -inf
+    const bool need = mnew > mref + kRescaleSlack;
+    if (__any(need)) {
+      const float alpha = need ? exp2f_hw(mref - mnew) : 1.0f;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      if (need) mref = mnew;
+    }
+    const float mu = mref == kNegInf ? 0.f : mref;
+    u32x4 pf[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = exp2f_hw(fmaf(sc[8 * kc + j], c2, -mu));
+      pf[kc] = u32x4{pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]),
+                     pack2<T>(p[6], p[7])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lsum = add_pair_ones<T>(pf[kc][e], ones, lsum);
+    }
+    // O^T += V^T P^T over the two 16-key chunks of the tile
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = mfma32<T>(ln.tr_frag(vt, kc * 16, db), pf[kc], oacc[db]);
+  }
+
+  // partial results of this key range (rows >= Nq are dropped by the buffer bounds)
+  const long part = ((long)(b * a.H + h) * a.S + s) * a.Nq;
+  const auto ro = make_rsrc(a.opart + part * D, (uint32_t)a.Nq * D * 4);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x16& x = oacc[db];
+      const u32x4 val = {__float_as_uint(x[4 * rr]), __float_as_uint(x[4 * rr + 1]),
+                         __float_as_uint(x[4 * rr + 2]), __float_as_uint(x[4 * rr + 3])};
+      buf_store16(ro, ((uint32_t)qi * D + db * 32 + 8 * rr + 4 * g) * 4, val);
+    }
+  const float l = pair_sum(lsum);
+  if (g == 0 && qi < a.Nq) {
+    a.mpart[part + qi] = mref;
+    a.lpart[part + qi] = l;
+  }
+}
+
+// One wave per output row (b, q, h): merge the S partials.
+template <int D, class T>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= (long)a.B * a.H * a.Nq) return;
+  const int qi = row % a.Nq;
+  const long bh = row / a.Nq;  // b * H + h
+  const int h = bh % a.H, b = bh / a.H;
+  const long part0 = bh * a.S * a.Nq + qi;
+  float m = kNegInf;
+  for (int s = 0; s < a.S; ++s) m = fmaxf(m, a.mpart[part0 + (long)s * a.Nq]);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float l = 0.f;
+  if (m != kNegInf) {
+    for (int s = 0; s < a.S; ++s) {
+      const long p = part0 + (long)s * a.Nq;
+      const float ls = a.lpart[p];
+      if (ls == 0.f) continue;
+      const float wgt = exp2f_hw(a.mpart[p] - m);
+      l += ls * wgt;
+      const float* op = a.opart + p * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += wgt * op[e];
+    }
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  uint16_t* o = a.o + (((long)b * a.Nq + qi) * a.H + h) * D + lane * PER;
+  if constexpr (PER == 2) {
+    *reinterpret_cast<uint32_t*>(o) = pack2<T>(acc[0] * inv, acc[1] * inv);
+  } else {
+    o[0] = (uint16_t)(pack2<T>(acc[0] * inv, 0.f) & 0xffffu);
+  }
+  if (lane == 0) a.lse[bh * a.Nq + qi] = l > 0.f ? (m + log2f_hw(l)) * kLn2 : kNegInf;
+}
+
+template <int D, class T, bool CAUSAL>
+hipError_t launch(const DecodeArgs& a, hipStream_t st) {
+  constexpr int kWaves = Cfg<D>::kWaves;
+  const long nqb = (a.Nq + 31) / 32;
+  const long G = (a.S + kWaves - 1) / kWaves;
+  const long grid1 = G * nqb * a.H * a.B;
+  hipLaunchKernelGGL((decode_kernel<D, T, CAUSAL>), dim3((unsigned)grid1), dim3(64 * kWaves),
+                     0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long rows = (long)a.B * a.H * a.Nq;
+  hipLaunchKernelGGL((combine_kernel<D, T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                     a);
+  return hipGetLastError();
+}
+
+template <int D, class T>
+hipError_t launch_c(const DecodeArgs& a, bool causal, hipStream_t st) {
+  return causal ? launch<D, T, true>(a, st) : launch<D, T, false>(a, st);
+}
+
+}  // namespace
+}  // namespace dec
+
+int decode_splits(int B, int Nq, int Nk, int H, int d, int requested) {
+  const long tiles = (Nk + dec::kTK - 1) / dec::kTK;  // at least one tile per range
+  long s = requested;
+  if (s <= 0) {
+    // about one workgroup per CU of a 256-CU part: long ranges keep each wave's stream of
+    // tiles going, which is what the HBM bandwidth needs
+    const long units = (long)B * H * ((Nq + 31) / 32);
+    const int nw = d == 128 ? dec::Cfg<128>::kWaves : dec::Cfg<64>::kWaves;
+    s = nw * ((256 + units - 1) / units);
+  }
+  if (s > tiles) s = tiles;
+  return (int)(s < 1 ? 1 : s);
+}
+
+int decode_span(int Nk, int splits) {
+  const int per = (Nk + splits - 1) / splits;
+  return (per + dec::kTK - 1) / dec::kTK * dec::kTK;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t st) {
+  if ((long)a.B * a.H * a.Nq == 0) return hipSuccess;
+  if (d == 128)
+    return bf16 ? dec::launch_c<128, BF16>(a, causal, st) : dec::launch_c<128, F16>(a, causal, st);
+  return bf16 ? dec::launch_c<64, BF16>(a, causal, st) : dec::launch_c<64, F16>(a, causal, st);
+}
+
+}  // namespace fa

@@ -83,3 +83,30 @@ WORKLOADS = {
     "train_causal_fwd_bwd": Workload("train_causal_fwd_bwd", 4, 4096, 16, 128, "bf16", True,
                                      backward=True),
 }
+
+
+def decode_inputs(B, Nq, Nk, H, d, dtype, seed):
+    """Q [B, Nq, H, d] and K, V [B, Nk, H, d] as uint16 bit patterns (seeds +0, +1, +2)."""
+    return (normal_bits((B, Nq, H, d), dtype, seed), normal_bits((B, Nk, H, d), dtype, seed + 1),
+            normal_bits((B, Nk, H, d), dtype, seed + 2))
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Nq: int  # query rows per sequence (the newest tokens)
+    Nk: int  # cached keys and values per sequence
+    H: int
+    d: int
+    dtype: str
+    causal: bool
+
+
+# Decode shapes: no page gives one, so these follow the benchmark's own sequences: one new
+# token after the 8192-token prefill of the long-sequence workload, and one new token against
+# the packed workload's 131072 tokens as a single long context.
+DECODE_WORKLOADS = {
+    "decode_8k": DecodeWorkload("decode_8k", 4, 1, 8192, 16, 128, "bf16", True),
+    "decode_128k": DecodeWorkload("decode_128k", 1, 1, 131072, 16, 128, "bf16", True),
+}

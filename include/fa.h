@@ -158,6 +158,34 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         int total_tokens, int max_seqlen, int H, int d, fa_dtype dtype,
                         float softmax_scale, int causal, hipStream_t stream);
 
+/*
+ * Split-KV forward for decode shapes: Nq query rows (e.g. the newest tokens of each
+ * sequence) against Nk cached keys and values. The keys are cut into num_splits contiguous
+ * ranges processed in parallel; each range is reduced to a partial (O, m, l) by the online
+ * softmax and the partials are combined with the block-merge rule of "FlashAttention 与算子
+ * 融合" (section on the two keys of FlashAttention): m = max m_s, l = sum l_s exp(m_s - m),
+ * O = sum O_s l_s exp(m_s - m) / l. The narration script ("FlashAttention 短片讲解稿",
+ * segment 适用范围与关键结论) singles this shape out as different from training and prefill.
+ *   q          : in,  [B, Nq, H, d], dtype
+ *   k, v       : in,  [B, Nk, H, d], dtype
+ *   o          : out, [B, Nq, H, d], dtype
+ *   lse        : out, fp32 [B, H, Nq]
+ *   workspace  : fa_fwd_splitkv_workspace_size(B, Nq, Nk, H, d, num_splits) bytes, 16-byte
+ *                aligned; its contents are overwritten
+ *   num_splits : key ranges per (b, h); 0 lets the library choose from the shape. Values
+ *                above ceil(Nk / 32) are lowered to it. 0 <= num_splits <= 4096.
+ *   causal     : query row i stands at position Nk - Nq + i and sees keys j <= Nk - Nq + i
+ *                (none when Nk - Nq + i < 0: such rows get O = 0 and lse = -inf). With
+ *                Nq = Nk this is fa_fwd's causal mask.
+ * B, Nq, H >= 0 (B*Nq*H == 0 is a no-op returning FA_OK); Nk >= 1.
+ * Limits: (Nk + 256) * H * d < 2^30 and (Nq + 256) * H * d < 2^30.
+ * Deterministic: a fixed num_splits gives identical bits on every call.
+ */
+size_t fa_fwd_splitkv_workspace_size(int B, int Nq, int Nk, int H, int d, int num_splits);
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         void* workspace, int B, int Nq, int Nk, int H, int d, fa_dtype dtype,
+                         float softmax_scale, int causal, int num_splits, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

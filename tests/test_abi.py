@@ -26,7 +26,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_prep",
-         "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen", "fa_bwd_varlen"])
+         "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen", "fa_bwd_varlen",
+         "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -119,3 +120,43 @@ def test_bwd_varlen_argument_checks(lib):
     bad[9] = None  # workspace
     assert lib.fa_bwd_varlen(*bad, FAKE, 2, 100, 64, 2, 64, 1, f, 1, None) == 1
     assert lib.fa_bwd_varlen(*a, FAKE, 2, 0, 64, 2, 64, 1, f, 1, None) == 0
+
+
+def test_splitkv_argument_checks(lib):
+    f = ctypes.c_float(0.1)
+    a = [FAKE] * 6  # q, k, v, o, lse, workspace
+
+    def call(*args, ptrs=a, scale=f):
+        B, Nq, Nk, H, d, dt, causal, ns = args
+        return lib.fa_fwd_splitkv(*ptrs, B, Nq, Nk, H, d, dt, scale, causal, ns, None)
+
+    assert call(-1, 1, 64, 2, 64, 1, 0, 0) == 1      # negative batch
+    assert call(1, 1, 0, 2, 64, 1, 0, 0) == 1        # no keys
+    assert call(1, 1, 64, 2, 64, 1, 0, -1) == 1      # negative split count
+    assert call(1, 1, 64, 2, 64, 1, 0, 4097) == 1    # too many splits
+    assert call(1, 1, 64, 2, 64, 7, 0, 0) == 1       # unknown dtype
+    assert call(1, 1, 64, 2, 64, 1, 0, 0, scale=ctypes.c_float(float("nan"))) == 1
+    assert call(1, 1, 64, 2, 72, 1, 0, 0) == 2       # head dim
+    assert call(1, 1, 1 << 24, 2, 128, 1, 0, 0) == 2  # key rows beyond the offset range
+    misaligned = list(a)
+    misaligned[0] = FAKE + 2
+    assert call(1, 1, 64, 2, 64, 1, 0, 0, ptrs=misaligned) == 1
+    no_ws = list(a)
+    no_ws[5] = None
+    assert call(1, 1, 64, 2, 64, 1, 0, 0, ptrs=no_ws) == 1
+    assert call(0, 1, 64, 2, 64, 1, 0, 0) == 0       # empty batch: nothing to do
+    assert call(1, 0, 64, 2, 64, 1, 1, 0) == 0       # no query rows: nothing to do
+
+
+def test_splitkv_workspace_size(lib):
+    """(d + 2) fp32 per (b, h, split, query row): linear in the query rows, and independent
+    of the number of keys beyond the split count."""
+    import exact_io_aware_10_amd as fa
+    ws = fa.fa_fwd_splitkv_workspace_size
+    assert ws(1, 1, 8192, 1, 128, 4) == 4 * (128 + 2) * 4
+    assert ws(4, 3, 8192, 16, 64, 8) == 4 * 16 * 8 * 3 * (64 + 2) * 4
+    assert ws(1, 1, 100, 1, 64, 50) == 4 * (64 + 2) * 4   # at most ceil(Nk / 32) ranges
+    assert ws(1, 1, 1 << 20, 1, 128, 4) == ws(1, 1, 1 << 12, 1, 128, 4)
+    auto = ws(4, 1, 8192, 16, 128, 0)
+    assert auto > 0 and auto % (4 * 16 * (128 + 2) * 4) == 0
+    assert ws(1, 1, 64, 1, 96, 0) == 0 and ws(-1, 1, 64, 1, 64, 0) == 0

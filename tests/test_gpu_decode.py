@@ -1,0 +1,94 @@
+"""GPU parity of fa_fwd_splitkv (split-KV decode forward) against the fp64 oracle (called
+through the C ABI via the ctypes binding)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_io_aware_10_amd import inputs
+from parity import assert_close, to_device, f64_of
+
+pytestmark = pytest.mark.gpu
+
+
+def fa():
+    import exact_io_aware_10_amd as m
+    return m
+
+
+def run(B, Nq, Nk, H, d, dtype, causal, splits, seed, scale=None):
+    print(f"[decode] B={B} Nq={Nq} Nk={Nk} H={H} d={d} {dtype} causal={causal} "
+          f"splits={splits} seed={seed} scale={scale}", flush=True)
+    qb, kb, vb = inputs.decode_inputs(B, Nq, Nk, H, d, dtype, seed)
+    q, k, v = (to_device(x, dtype) for x in (qb, kb, vb))
+    o, lse = fa().fa_fwd_splitkv(q, k, v, causal=causal, softmax_scale=scale,
+                                 num_splits=splits)
+    import torch
+    torch.cuda.synchronize()
+    return (qb, kb, vb), f64_of(o, dtype), lse.cpu().numpy().astype(np.float64)
+
+
+def check(ins, o, lse, dtype, causal, scale, rtol=0.0):
+    qb, kb, vb = ins
+    d = qb.shape[-1]
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    w = lambda x: oracle.widen(x, dtype)
+    ro, rlse = oracle.fwd_decode(w(qb), w(kb), w(vb), scale, causal)
+    assert_close("O", o, ro, rtol=rtol)
+    # rows that see no key: lse = -inf on both sides, O = 0 (checked above)
+    empty = np.isneginf(rlse)
+    assert np.array_equal(np.isneginf(lse), empty)
+    assert_close("LSE", np.where(empty, 0.0, lse), np.where(empty, 0.0, rlse), rtol=rtol)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Nq,Nk,H,splits", [(1, 1, 1, 1, 0), (2, 1, 1000, 3, 0),
+                                               (2, 1, 1000, 3, 1), (1, 1, 1000, 2, 7),
+                                               (1, 5, 300, 2, 0), (1, 33, 1024, 1, 3),
+                                               (2, 71, 200, 2, 0)])
+def test_decode_small(B, Nq, Nk, H, splits, d, dtype, causal):
+    ins, o, lse = run(B, Nq, Nk, H, d, dtype, causal, splits, seed=Nq + Nk + d)
+    check(ins, o, lse, dtype, causal, None)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_more_queries_than_keys(causal):
+    # causal: the first Nq - Nk rows stand before the first key and see none
+    ins, o, lse = run(1, 40, 17, 2, 64, "bf16", causal, 0, seed=11)
+    check(ins, o, lse, "bf16", causal, None)
+    if causal:
+        assert np.all(o[:, :23] == 0.0) and np.all(np.isneginf(lse[:, :, :23]))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 32, 4096])
+def test_decode_split_counts(splits):
+    # any cut of the keys, including more ranges than tiles (lowered) and empty ranges
+    for Nk in (64, 321):
+        ins, o, lse = run(2, 3, Nk, 2, 128, "bf16", True, splits, seed=Nk + splits)
+        check(ins, o, lse, "bf16", True, None)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.5])
+def test_decode_scale_values(scale):
+    ins, o, lse = run(1, 4, 500, 2, 64, "bf16", True, 0, seed=7, scale=scale)
+    check(ins, o, lse, "bf16", True, scale, rtol=2.0 ** -7)
+
+
+def test_decode_deterministic():
+    import torch
+    qb, kb, vb = inputs.decode_inputs(2, 3, 2000, 4, 128, "bf16", 3)
+    q, k, v = (to_device(x, "bf16") for x in (qb, kb, vb))
+    o1, l1 = fa().fa_fwd_splitkv(q, k, v, causal=True, num_splits=12)
+    o2, l2 = fa().fa_fwd_splitkv(q, k, v, causal=True, num_splits=12)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", sorted(inputs.DECODE_WORKLOADS))
+def test_decode_workloads(name):
+    wl = inputs.DECODE_WORKLOADS[name]
+    ins, o, lse = run(wl.B, wl.Nq, wl.Nk, wl.H, wl.d, wl.dtype, wl.causal, 0, seed=0)
+    check(ins, o, lse, wl.dtype, wl.causal, None)
