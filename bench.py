@@ -42,6 +42,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak (vendor figure, no spar
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E peak bandwidth (vendor figure)
 CSRC = os.path.join(ROOT, "exact_io_aware_10_amd", "csrc")
 KERNEL_SOURCES = {  # the files whose text determines each kernel's code (build.py: flags)
+    "decode_kernel": ["fa_decode.hip", "fa_decode.h", "fa_bwd_common.h", "fa_device.h",
+                      "fa_internal.h", "../build.py"],
     "fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_internal.h", "../build.py"],
     "bwd_prep_kernel": ["fa_bwd.hip", "fa_bwd_common.h", "fa_device.h", "fa_internal.h",
                         "../build.py"],
@@ -110,7 +112,12 @@ def measured_traffic(kernel):
     profiles/<kernel>_long_seq_traffic.txt (FETCH_SIZE and WRITE_SIZE, each scaled by what
     the same counter reads for a plain copy of known size), or None when that summary is
     missing or was taken on other kernel source than the current one."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_long_seq_traffic.txt")
+    return measured_traffic_for(f"{kernel}_long_seq", kernel)
+
+
+def measured_traffic_for(stem, kernel):
+    """measured_traffic for the summary profiles/<stem>_traffic.txt."""
+    path = os.path.join(ROOT, "profiles", f"{stem}_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -160,8 +167,8 @@ def rocprof_summary(paths):
                     print(f"  {cn:<32} {val:>16.1f} per dispatch ({n} samples)  {name[:80]}")
 
 
-def _counter_avgs(db_path, counter):
-    """{kernel name: mean per-dispatch value of `counter`} from one rocprofv3 database."""
+def _counter_values(db_path, counter):
+    """{kernel name: [per-dispatch values of `counter`]} from one rocprofv3 database."""
     import glob
     import sqlite3
     dbs = (glob.glob(os.path.join(db_path, "**", "*.db"), recursive=True)
@@ -169,35 +176,52 @@ def _counter_avgs(db_path, counter):
     out = {}
     for db in dbs:
         c = sqlite3.connect(db)
-        for name, val in c.execute("select kernel_name, avg(value) from counters_collection "
-                                   "where counter_name = ? group by kernel_name", (counter,)):
-            out[name] = val
+        cols = [r[1] for r in c.execute("pragma table_info(counters_collection)")]
+        key = "dispatch_id" if "dispatch_id" in cols else "rowid"
+        for name, val in c.execute(f"select kernel_name, sum(value) from counters_collection "
+                                   f"where counter_name = ? group by {key}, kernel_name",
+                                   (counter,)):
+            out.setdefault(name, []).append(val)
     return out
 
 
-def traffic_summary(fetch_db, write_db, kernel, mib):
-    """HBM bytes per launch of `kernel`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-    scaled by (known bytes of the calibration copy) / (what the same counter read for it)."""
-    fetch = _counter_avgs(fetch_db, "FETCH_SIZE")
-    write = _counter_avgs(write_db, "WRITE_SIZE")
-    pick = lambda d, key: next(v for k, v in d.items() if key in k)
+def traffic_summary(fetch_db, write_db, kernels, mib):
+    """HBM bytes per launch of the kernels named in `kernels` (comma-separated; the first names
+    the source hash), summed: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the
+    dispatches of each kernel), each scaled by (known bytes of the calibration copy) / (what the
+    same counter read for it). The calibration copy is the largest copyBuffer dispatch of the
+    run; smaller ones are the program's own host-to-device copies."""
+    fetch = _counter_values(fetch_db, "FETCH_SIZE")
+    write = _counter_values(write_db, "WRITE_SIZE")
+    names = kernels.split(",")
+
+    def pick(d, key):
+        vals = [v for k, vs in d.items() if key in k for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of {key} in the counter database")
+        return vals
+
     copy_bytes = mib * (1 << 20)
-    f_fetch = copy_bytes / (pick(fetch, "copyBuffer") * 1024)
-    f_write = copy_bytes / (pick(write, "copyBuffer") * 1024)
-    kf, kw = pick(fetch, kernel), pick(write, kernel)
-    total = kf * 1024 * f_fetch + kw * 1024 * f_write
-    print(f"kernel: {kernel}")
-    print(f"kernel_source_sha256_16: {kernel_source_hash(kernel)}")
+    cf, cw = max(pick(fetch, "copyBuffer")), max(pick(write, "copyBuffer"))
+    f_fetch, f_write = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    print(f"kernel: {kernels}")
+    print(f"kernel_source_sha256_16: {kernel_source_hash(names[0])}")
     print(f"calibration_copy_bytes: {copy_bytes}")
-    print(f"copy_fetch_size_kib: {pick(fetch, 'copyBuffer'):.1f}")
-    print(f"copy_write_size_kib: {pick(write, 'copyBuffer'):.1f}")
+    print(f"copy_fetch_size_kib: {cf:.1f}")
+    print(f"copy_write_size_kib: {cw:.1f}")
     print(f"fetch_scale: {f_fetch:.4f}")
     print(f"write_scale: {f_write:.4f}")
-    print(f"fetch_size_kib_per_dispatch: {kf:.1f}")
-    print(f"write_size_kib_per_dispatch: {kw:.1f}")
-    print(f"hbm_read_bytes_per_launch: {kf * 1024 * f_fetch:.0f}")
-    print(f"hbm_write_bytes_per_launch: {kw * 1024 * f_write:.0f}")
-    print(f"hbm_bytes_per_launch: {total:.0f}")
+    rd = wr = 0.0
+    for n in names:
+        kf, kw = pick(fetch, n), pick(write, n)
+        kf, kw = sum(kf) / len(kf), sum(kw) / len(kw)
+        print(f"{n}.fetch_size_kib_per_dispatch: {kf:.1f}")
+        print(f"{n}.write_size_kib_per_dispatch: {kw:.1f}")
+        rd += kf * 1024 * f_fetch
+        wr += kw * 1024 * f_write
+    print(f"hbm_read_bytes_per_launch: {rd:.0f}")
+    print(f"hbm_write_bytes_per_launch: {wr:.0f}")
+    print(f"hbm_bytes_per_launch: {rd + wr:.0f}")
 
 
 def copy_calibration(mib):
@@ -211,6 +235,82 @@ def copy_calibration(mib):
     b.copy_(a)
     torch.cuda.synchronize()
     del a, b
+
+
+def decode_bytes(B, Nq, Nk, H, d):
+    """Compulsory bytes of one split-KV decode call: K and V once, Q and O once (2 bytes per
+    element), LSE (4 bytes per row)."""
+    return 2.0 * 2 * B * Nk * H * d + 2.0 * 2 * B * Nq * H * d + 4.0 * B * H * Nq
+
+
+def decode_cpu_baseline(wl, bits, min_s=10.0):
+    """The fp64 oracle on the whole decode workload, repeated for at least min_s seconds."""
+    import oracle
+    w = [oracle.widen(x, wl.dtype) for x in bits]
+    nth = oracle.default_threads()
+    scale = 1 / np.sqrt(wl.d)
+    reps, secs = 0, 0.0
+    while secs < min_s:
+        t0 = time.perf_counter()
+        oracle.fwd_decode(w[0], w[1], w[2], scale, wl.causal, nthreads=nth)
+        secs += time.perf_counter() - t0
+        reps += 1
+    rate = decode_bytes(wl.B, wl.Nq, wl.Nk, wl.H, wl.d) * reps / secs / 1e9
+    return {"value": round(rate, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": f"fp64 oracle decode of the whole workload, {reps} runs in {secs:.1f} s "
+                      f"on {nth} host threads"}
+
+
+def decode_main(args):
+    """One JSON line for a decode workload: fa_fwd_splitkv (decode kernel + combine kernel)
+    timed with HIP events on its stream, as HBM bandwidth of the compulsory bytes."""
+    import torch
+    import exact_io_aware_10_amd as fa
+    from exact_io_aware_10_amd import inputs
+
+    if args.workload not in inputs.DECODE_WORKLOADS:
+        print(f"unknown workload {args.workload}", file=sys.stderr)
+        sys.exit(2)
+    wl = inputs.DECODE_WORKLOADS[args.workload]
+    B, Nq, Nk, H, d = wl.B, wl.Nq, wl.Nk, wl.H, wl.d
+    bits = inputs.decode_inputs(B, Nq, Nk, H, d, wl.dtype, 0)
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in bits)
+    ws = torch.empty(max(fa.fa_fwd_splitkv_workspace_size(B, Nq, Nk, H, d, 0), 16),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda: fa.fa_fwd_splitkv(q, k, v, causal=wl.causal, num_splits=0, workspace=ws)
+    for _ in range(max(args.warmup, 10)):
+        call()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 50)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    nbytes = decode_bytes(B, Nq, Nk, H, d)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    splits = fa.fa_fwd_splitkv_workspace_size(B, Nq, Nk, H, d, 0) // (B * H * Nq * (d + 2) * 4)
+    out = {
+        "metric": f"split-KV decode HBM GB/s of compulsory bytes, B{B} Nq{Nq} Nk{Nk} H{H} d{d} "
+                  f"bf16",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": max(args.warmup, 10), "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "Nq": Nq, "Nk": Nk, "H": H, "d": d,
+                   "causal": wl.causal, "splits": int(splits),
+                   "step": "fa_fwd_splitkv (decode kernel + combine kernel)"},
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel + combine_kernel",
+                     "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic_for(f"splitkv_{wl.name}", "decode_kernel"),
+                     "avg_launch_ms": round(ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = decode_cpu_baseline(wl, bits)
+    print(json.dumps(out))
 
 
 def main():
@@ -228,6 +328,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--workload", default=WORKLOAD["name"],
+                    help="long_seq_fwd_bwd (default) or a decode workload: decode_8k, "
+                         "decode_128k")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -241,6 +344,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+    if args.workload != WORKLOAD["name"]:
+        decode_main(args)
+        return
     wl = WORKLOAD
     B, N, H, d, dtype, causal = wl["B"], wl["N"], wl["H"], wl["d"], wl["dtype"], wl["causal"]
     dev = torch.device("cuda:0")
