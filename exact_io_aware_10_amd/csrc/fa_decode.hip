@@ -10,12 +10,12 @@
 // Query row i stands at position Nk - Nq + i of the sequence; the causal mask hides keys
 // after it (for Nq = Nk this is the ordinary causal mask).
 //
-// Kernel 1 (decode_kernel): a workgroup is four independent waves, one key range each, over
-// one block of 32 query rows of one (b, h). A wave holds the Q rows as MFMA B operands and
-// streams its range in 32-key tiles of K and V from HBM straight into its own part of LDS
-// (buffer_load_dwordx4 ... lds, double buffered, issued from inline assembly so that the
-// compiler does not turn its conservative aliasing waits into a wait for the next tile; the
-// wave waits for each tile itself). S^T = K Q^T and O^T += V^T P^T on MFMA as in the forward
+// Kernel 1 (decode_kernel): a workgroup is two (d = 128) or four (d = 64) independent waves,
+// one key range each, over one block of 32 query rows of one (b, h). A wave holds the Q rows
+// as MFMA B operands and streams its range in 32-key tiles of K and V from HBM straight into
+// its own part of LDS (buffer_load_dwordx4 ... lds into a ring of four buffers, three tiles in
+// flight, issued from inline assembly so that the compiler does not turn its conservative
+// aliasing waits into a wait for the next tile; the wave waits for each tile itself). S^T = K Q^T and O^T += V^T P^T on MFMA as in the forward
 // (the matrix cores have ample headroom at these shapes: the bound is the K/V stream).
 // Tiles use the dual chunk swizzle of the backward kernels, which keeps both the row-fragment
 // reads of K and the transposed reads of V conflict-free.
