@@ -39,12 +39,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak (vendor figure, no sparsity)
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA peak (vendor figure, no sparsity)
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E peak bandwidth (vendor figure)
 CSRC = os.path.join(ROOT, "exact_io_aware_10_amd", "csrc")
 KERNEL_SOURCES = {  # the files whose text determines each kernel's code (build.py: flags)
     "decode_kernel": ["fa_decode.hip", "fa_decode.h", "fa_bwd_common.h", "fa_device.h",
                       "fa_internal.h", "../build.py"],
     "fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_internal.h", "../build.py"],
+    "fwd_fp8_kernel": ["fa_fwd_fp8.hip", "fa_device.h", "fa_internal.h", "../build.py"],
     "bwd_prep_kernel": ["fa_bwd.hip", "fa_bwd_common.h", "fa_device.h", "fa_internal.h",
                         "../build.py"],
     "bwd_dkdv_kernel": ["fa_bwd_dkdv.hip", "fa_bwd_common.h", "fa_device.h", "fa_internal.h",
@@ -313,6 +315,78 @@ def decode_main(args):
     print(json.dumps(out))
 
 
+def fp8_cpu_baseline(wl, codes, descales, min_s=10.0, max_slices=16):
+    """The fp64 oracle's FP8 forward (widen the e4m3 codes, apply the descales, plain
+    definition) on whole (b, h) slices of the benchmark's inputs, for at least min_s
+    seconds or max_slices slices; algorithmic TFLOP/s of the forward."""
+    import oracle
+    nth = oracle.default_threads()
+    scale = 1 / math.sqrt(wl.d)
+    done, secs = 0, 0.0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            if secs >= min_s or done >= max_slices:
+                break
+            sl = [np.ascontiguousarray(c[b:b + 1, :, h:h + 1, :]) for c in codes]
+            t0 = time.perf_counter()
+            oracle.fwd_fp8(*sl, *descales, scale, wl.causal, nthreads=nth)
+            secs += time.perf_counter() - t0
+            done += 1
+    flops = done * fwd_flops(1, wl.N, 1, wl.d, wl.causal)
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": nth,
+            "kind": "oracle",
+            "sample": f"fp64 oracle FP8 forward of {done} of the {wl.B * wl.H} (b,h) slices "
+                      f"of the benchmark's inputs (N={wl.N}, d={wl.d}), {secs:.1f} s on {nth} "
+                      f"host threads"}
+
+
+def fp8_main(args):
+    """One JSON line for an FP8 forward workload: fa_fwd_fp8 timed with HIP events on its
+    stream; algorithmic forward FLOP/s against the dense fp8 MFMA peak."""
+    import torch
+    import exact_io_aware_10_amd as fa
+    from exact_io_aware_10_amd import inputs
+
+    wl = inputs.FP8_WORKLOADS[args.workload]
+    B, N, H, d = wl.B, wl.N, wl.H, wl.d
+    codes, ds = inputs.fp8_inputs(B, N, H, d, 0)
+    q, k, v = (torch.from_numpy(c).cuda() for c in codes)
+    o = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    call = lambda: fa.fa_fwd_fp8(q, k, v, *ds, causal=wl.causal, out=o, lse=lse)
+    for _ in range(max(args.warmup, 5)):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    ff = fwd_flops(B, N, H, d, wl.causal)
+    tflops = ff / (ms * 1e-3) / 1e12
+    out = {
+        "metric": f"attention TFLOP/s fwd, B{B} H{H} N{N} d{d} fp8 e4m3 inputs, bf16 output"
+                  + (", causal" if wl.causal else ""),
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": max(args.warmup, 5), "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "N": N, "H": H, "d": d, "causal": wl.causal,
+                   "step": "fa_fwd_fp8"},
+        "roofline": {"bound": "mfma", "kernel": "fwd_fp8_kernel", "achieved": round(tflops, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic_for(f"fwd_fp8_kernel_{wl.name}",
+                                                     "fwd_fp8_kernel"),
+                     "avg_launch_ms": round(ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = fp8_cpu_baseline(wl, codes, ds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     if "--rocprof-summary" in sys.argv:
         rocprof_summary(sys.argv[sys.argv.index("--rocprof-summary") + 1:])
@@ -329,8 +403,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--workload", default=WORKLOAD["name"],
-                    help="long_seq_fwd_bwd (default) or a decode workload: decode_8k, "
-                         "decode_128k")
+                    help="long_seq_fwd_bwd (default), a decode workload (decode_8k, "
+                         "decode_128k) or an FP8 forward workload (long_seq_fp8, "
+                         "long_seq_causal_fp8)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -344,6 +419,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+    if args.workload in inputs.FP8_WORKLOADS:
+        fp8_main(args)
+        return
     if args.workload != WORKLOAD["name"]:
         decode_main(args)
         return

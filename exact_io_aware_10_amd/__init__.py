@@ -8,16 +8,20 @@ current HIP stream. There is no fallback: if the library is missing the calls ra
     dq, dk, dv = fa_bwd(q, k, v, o, lse, dout, causal=False, softmax_scale=None)
     o, lse = fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, softmax_scale=None)
     o, lse = fa_fwd_splitkv(q, k, v, causal=False, softmax_scale=None, num_splits=0)
+    o, lse = fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False,
+                        softmax_scale=None)
 
 q, k, v, o, dout: [B, N, H, d] (packed: [T, H, d]) contiguous bf16 or fp16 CUDA tensors;
 lse: fp32 [B, H, N] (packed: [H, T]); d in {64, 128}; softmax_scale defaults to 1/sqrt(d).
+fa_fwd_fp8 takes e4m3 tensors (torch.float8_e4m3fn, or uint8 holding the codes) with one
+float descale per tensor and returns a bf16 output.
 """
 import ctypes
 import math
 import os
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen",
-           "fa_bwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+           "fa_bwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_fp8",
            "fa_bwd_workspace_size", "fa_status_string", "FAError", "library_path",
            "load_library"]
 
@@ -63,6 +67,8 @@ def load_library():
     lib.fa_fwd_splitkv_workspace_size.restype = s
     lib.fa_fwd_splitkv.argtypes = [vp] * 6 + [i, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp] * 5 + [i, i, i, i, f, f, f, f, i, vp]
+    lib.fa_fwd_fp8.restype = i
     _lib = lib
     return lib
 
@@ -128,6 +134,32 @@ def fa_fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None):
                     _stream(q.device))
     if rc != FA_OK:
         raise FAError("fa_fwd", rc)
+    return o, lse
+
+
+def fa_fwd_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=False,
+               softmax_scale=None, out=None, lse=None):
+    """FP8 forward: q, k, v hold e4m3 codes ([B, N, H, d], torch.float8_e4m3fn or uint8),
+    each tensor's value being its descale times the codes' values. Returns (o bf16
+    [B,N,H,d], lse fp32 [B,H,N])."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N, H, d]")
+    if q.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"unsupported dtype {q.dtype}; expected float8_e4m3fn or uint8")
+    B, N, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype, q.device)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("out", o, q.shape, torch.bfloat16, q.device)
+    _check_tensor("lse", lse, (B, H, N), torch.float32, q.device)
+    rc = lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, N, H, d, float(q_descale), float(k_descale), float(v_descale),
+                        _scale(softmax_scale, d), int(bool(causal)), _stream(q.device))
+    if rc != FA_OK:
+        raise FAError("fa_fwd_fp8", rc)
     return o, lse
 
 

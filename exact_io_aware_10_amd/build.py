@@ -36,6 +36,7 @@ CFLAGS = [
 FILE_FLAGS = {
     "fa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fa_fwd.hip": ["-fno-honor-nans"],
+    "fa_fwd_fp8.hip": ["-fno-honor-nans"],
 }
 
 

@@ -81,6 +81,36 @@ FA_EXPORT fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
   return to_status(fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, false, stream));
 }
 
+FA_EXPORT fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o,
+                               float* lse, int B, int N, int H, int d, float q_descale,
+                               float k_descale, float v_descale, float softmax_scale,
+                               int causal, hipStream_t stream) {
+  // the size limits of the 16-bit path are kept (they bound element counts, so they also
+  // cover the one-byte rows)
+  fa_status st = check_common(B, N, H, d, FA_BF16, softmax_scale);
+  if (st != FA_OK) return st;
+  for (float x : {q_descale, k_descale, v_descale})
+    if (!(isfinite(x) && x > 0.f)) return FA_ERR_INVALID_ARG;
+  const float c = fabsf(softmax_scale) * q_descale * k_descale * kLog2e;
+  if (!isfinite(c)) return FA_ERR_INVALID_ARG;
+  if ((long)B * N * H == 0) return FA_OK;
+  if (!tensors_ok({q, k, v, o}) || lse == nullptr || ((uintptr_t)lse & 3u))
+    return FA_ERR_INVALID_ARG;
+  fa::Fp8FwdArgs a{};
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.scale_log2 = fmaxf(c, FLT_MIN);
+  a.qsign = softmax_scale < 0.f ? 0x80808080u : 0u;
+  a.v_descale = v_descale;
+  return to_status(fa::launch_fwd_fp8(a, d, causal != 0, stream));
+}
+
 FA_EXPORT size_t fa_bwd_workspace_size(int B, int N, int H, int d) {
   if (B < 0 || N < 0 || H < 0 || (d != 64 && d != 128)) return 0;
   return (size_t)8 * B * H * N;

@@ -40,6 +40,22 @@ struct BwdArgs {
   uint32_t qsign;
 };
 
+// One FP8 forward launch (dense). q, k, v: e4m3 codes [B, N, H, d]; o: bf16; lse: fp32.
+struct Fp8FwdArgs {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  uint16_t* o;
+  float* lse;
+  int B, N, H;
+  float scale_log2;  // |softmax_scale| * q_descale * k_descale * log2(e)
+  uint32_t qsign;    // 0x80808080 flips the sign of q (negative softmax_scale), else 0
+  float v_descale;
+};
+
+__attribute__((visibility("hidden"))) hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, int d,
+                                                                bool causal,
+                                                                hipStream_t stream);
 __attribute__((visibility("hidden"))) hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16,
                                                             bool causal, bool varlen,
                                                             hipStream_t stream);

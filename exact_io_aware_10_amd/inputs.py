@@ -8,6 +8,11 @@ lengths and names the five workloads.
 
 Seeds: Q, K, V and dO use default_rng(seed + 0, 1, 2, 3); sequence lengths use
 default_rng(seed + 4).
+
+FP8 inputs draw the same N(0, 1) values and store each tensor as OCP FP8 E4M3 codes with one
+per-tensor descale factor: descale = amax / 448 (448 is e4m3's largest finite value) in
+fp32, code = e4m3(x / descale) rounded to nearest even. The value the attention sees is
+descale * (code's value).
 """
 from dataclasses import dataclass
 from typing import Optional
@@ -25,6 +30,42 @@ def round_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f16":
         return x.astype(np.float16).view(np.uint16)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _e4m3_positive_values() -> np.ndarray:
+    """Values of the e4m3 codes 0x00..0x7E (sign 0): 1 sign, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; 0x7F is NaN."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (8 + m) * 2.0 ** (e - 10.0))
+
+
+def round_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """fp32 array -> uint8 e4m3 codes, round to nearest even (ties to the even code),
+    magnitudes above 448 saturated to 448."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    vals = _e4m3_positive_values()
+    a = np.minimum(np.abs(x).astype(np.float64), vals[-1])
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return code | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))
+
+
+def fp8_tensor(shape, seed: int):
+    """One N(0, 1) tensor as (e4m3 codes uint8, descale float) with descale = amax / 448."""
+    x = np.random.default_rng(seed).standard_normal(size=shape, dtype=np.float32)
+    amax = float(np.abs(x).max()) if x.size else 1.0
+    descale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    return round_to_e4m3(x / descale), float(descale)
+
+
+def fp8_inputs(B, N, H, d, seed):
+    """Q, K, V as e4m3 codes [B, N, H, d] (seeds +0, +1, +2) and their descale factors."""
+    qs = [fp8_tensor((B, N, H, d), seed + i) for i in range(3)]
+    return [c for c, _ in qs], [s for _, s in qs]
 
 
 def normal_bits(shape, dtype: str, seed: int) -> np.ndarray:
@@ -85,6 +126,14 @@ WORKLOADS = {
 }
 
 
+# FP8 forward workloads (e4m3 inputs, bf16 output): the long-sequence shape, without and
+# with the causal mask.
+FP8_WORKLOADS = {
+    "long_seq_fp8": Workload("long_seq_fp8", 4, 8192, 16, 128, "e4m3", False),
+    "long_seq_causal_fp8": Workload("long_seq_causal_fp8", 4, 8192, 16, 128, "e4m3", True),
+}
+
+
 def decode_inputs(B, Nq, Nk, H, d, dtype, seed):
     """Q [B, Nq, H, d] and K, V [B, Nk, H, d] as uint16 bit patterns (seeds +0, +1, +2)."""
     return (normal_bits((B, Nq, H, d), dtype, seed), normal_bits((B, Nk, H, d), dtype, seed + 1),
@@ -103,9 +152,9 @@ class DecodeWorkload:
     causal: bool
 
 
-# Decode shapes: no page gives one, so these follow the benchmark's own sequences: one new
-# token after the 8192-token prefill of the long-sequence workload, and one new token against
-# the packed workload's 131072 tokens as a single long context.
+# Decode shapes: one new token after the wiki's batch 4 x 16 heads x 8k sequences, and one
+# new token against a single 128k-token context (the long row of the wiki's comparison of
+# standard and tiled attention).
 DECODE_WORKLOADS = {
     "decode_8k": DecodeWorkload("decode_8k", 4, 1, 8192, 16, 128, "bf16", True),
     "decode_128k": DecodeWorkload("decode_128k", 1, 1, 131072, 16, 128, "bf16", True),

@@ -71,6 +71,29 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  hipStream_t stream);
 
 /*
+ * FP8 forward: the forward above with q, k, v stored as OCP FP8 E4M3 codes ("e4m3fn": 1 sign,
+ * 4 exponent (bias 7), 3 mantissa bits; largest finite 448; no infinities) and one fp32
+ * descale factor per tensor, so that the value of an element is descale * (code's value).
+ * "FlashAttention 与算子融合" (代际演进 table, 工程实践 precision note) names FP8 as the path
+ * FlashAttention-3 adds; the per-tensor descales and the output type are this library's.
+ *   q, k, v : in,  [B, N, H, d], one byte per element (e4m3 codes), 16-byte aligned
+ *   o       : out, [B, N, H, d], bf16
+ *   lse     : out, fp32 [B, H, N], the log-sum-exp of the scaled scores
+ *             softmax_scale * q_descale * k_descale * <q_i, k_j>
+ * Computes O = v_descale * softmax(softmax_scale * q_descale * k_descale * Q K^T
+ * [+ causal mask]) V with both products on the FP8 matrix cores (fp32 accumulation) and P
+ * rounded to e4m3 (nearest even) before P V; the row sums add exactly those rounded values.
+ * q_descale, k_descale, v_descale must be finite and > 0 (else FA_ERR_INVALID_ARG), as must
+ * their product with |softmax_scale|; the other arguments and limits are fa_fwd's. The
+ * per-element error against exact attention of the stored values is bounded by P's rounding:
+ * each weight's relative error is at most 2^-4 (absolute 2^-10 of the row's largest weight
+ * below e4m3's normal range), plus the bf16 rounding of the output.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int N, int H, int d, float q_descale, float k_descale, float v_descale,
+                     float softmax_scale, int causal, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs: 8 * B * H * N (two fp32 row terms per query:
  * -D_i = -<dO_i, O_i> and -LSE_i * log2(e)). Linear in N: the backward never stores an
  * N x N matrix. Returns 0 for arguments fa_bwd would reject as sizes (negative sizes or a

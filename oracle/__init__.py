@@ -61,11 +61,19 @@ def default_threads() -> int:
 
 
 def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact fp64 value of stored 16-bit floats given as uint16 bit patterns.
+    """Exact fp64 value of stored floats given as bit patterns.
 
-    bf16 is the upper half of an IEEE binary32; fp16 is IEEE binary16. Both widen to
-    binary64 without rounding.
+    bf16 is the upper half of an IEEE binary32; fp16 is IEEE binary16 (both as uint16).
+    e4m3 is the OCP FP8 E4M3 format (uint8): sign bit, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN and
+    there are no infinities (largest finite 448). All widen to binary64 without rounding.
     """
+    if dtype == "e4m3":
+        b = np.ascontiguousarray(bits, dtype=np.uint8).astype(np.int64)
+        e, m = (b >> 3) & 15, b & 7
+        mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+        mag = np.where((e == 15) & (m == 7), np.nan, mag)
+        return np.where(b >> 7, -mag, mag)
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     if dtype == "bf16":
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -98,6 +106,16 @@ def fwd(q, k, v, scale, causal, nthreads=None):
                             int(bool(causal)), nthreads or default_threads())
     _check(rc, "oracle_fwd")
     return o, lse
+
+
+def fwd_fp8(q_codes, k_codes, v_codes, q_descale, k_descale, v_descale, scale, causal,
+            nthreads=None):
+    """Attention of FP8-stored tensors: each tensor's value is its descale times the e4m3
+    code's value (widened exactly), then the plain definition in fp64. Returns (O, LSE)."""
+    q = widen(q_codes, "e4m3") * float(q_descale)
+    k = widen(k_codes, "e4m3") * float(k_descale)
+    v = widen(v_codes, "e4m3") * float(v_descale)
+    return fwd(q, k, v, scale, causal, nthreads)
 
 
 def fwd_blocked(q, k, v, scale, causal, block_q, block_k, form, nthreads=None):

@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_prep",
          "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen", "fa_bwd_varlen",
-         "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv"])
+         "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv", "fa_fwd_fp8"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -160,3 +160,27 @@ def test_splitkv_workspace_size(lib):
     auto = ws(4, 1, 8192, 16, 128, 0)
     assert auto > 0 and auto % (4 * 16 * (128 + 2) * 4) == 0
     assert ws(1, 1, 64, 1, 96, 0) == 0 and ws(-1, 1, 64, 1, 64, 0) == 0
+
+
+def test_fp8_argument_checks(lib):
+    c = ctypes.c_float
+
+    def call(q=FAKE, lse=FAKE, B=1, N=8, H=1, d=64, qd=1.0, kd=1.0, vd=1.0, scale=0.125,
+             causal=0):
+        return lib.fa_fwd_fp8(q, FAKE, FAKE, FAKE, lse, B, N, H, d, c(qd), c(kd), c(vd),
+                              c(scale), causal, None)
+
+    assert call(q=None) == 1
+    assert call(q=FAKE + 8) == 1                  # misaligned
+    assert call(lse=None) == 1
+    assert call(B=-1) == 1
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(qd=bad) == 1
+        assert call(kd=bad) == 1
+        assert call(vd=bad) == 1
+    assert call(scale=float("nan")) == 1
+    assert call(qd=1e30, kd=1e30) == 1            # exponent scale overflows
+    assert call(d=96) == 2
+    assert call(N=1 << 20, H=64, d=128) == 2
+    assert call(B=0) == 0
+    assert call(q=None, N=0) == 0

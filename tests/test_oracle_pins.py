@@ -425,3 +425,133 @@ def test_decode_shift_invariance_and_large_scores():
         o2, lse2 = oracle.fwd_decode_split(q2, k2, v2, 1.0, causal, 4)
         np.testing.assert_allclose(o2[..., :8], o, rtol=0, atol=1e-11)
         np.testing.assert_allclose(lse2, lse + c, rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------- FP8 (e4m3) storage
+
+def test_e4m3_codes():
+    """Values the OCP E4M3 format fixes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits, no infinities): zero, the subnormals m * 2^-9, the smallest normal 2^-6, one,
+    the largest finite 448, NaN at S.1111.111."""
+    w = oracle.widen(np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0x3F, 0x40, 0x77, 0x78,
+                               0x7E, 0xFE, 0xB8], dtype=np.uint8), "e4m3")
+    want = [0.0, -0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.875, 2.0, 240.0, 256.0,
+            448.0, -448.0, -1.0]
+    assert list(w) == want
+    assert np.signbit(w[1])
+    assert np.isnan(oracle.widen(np.array([0x7F, 0xFF], dtype=np.uint8), "e4m3")).all()
+    allv = oracle.widen(np.arange(256, dtype=np.uint8), "e4m3")
+    pos = allv[:127]
+    assert np.all(np.diff(pos) > 0)                      # codes 0..126 increase strictly
+    assert np.array_equal(allv[128:255], -pos)           # sign bit mirrors
+    assert np.isfinite(allv).sum() == 254
+
+
+def test_e4m3_widen_matches_torch():
+    """Library cross-check: torch's float8_e4m3fn decodes every code to the same value."""
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    w = oracle.widen(codes, "e4m3")
+    assert np.array_equal(np.isnan(w), np.isnan(t))
+    assert np.array_equal(w[~np.isnan(w)], t[~np.isnan(t)])
+
+
+def test_e4m3_input_rounding():
+    """The input quantiser rounds to the nearest code, ties to the even code, and saturates
+    at 448; it agrees with torch's conversion."""
+    vals = oracle.widen(np.arange(127, dtype=np.uint8), "e4m3")
+    mids = (vals[:-1] + vals[1:]) / 2
+    got = oracle.widen(inputs.round_to_e4m3(mids.astype(np.float32)), "e4m3")
+    lo, hi = np.arange(126), np.arange(1, 127)
+    even = np.where(lo % 2 == 0, lo, hi)
+    assert np.array_equal(got, vals[even])
+    assert oracle.widen(inputs.round_to_e4m3(np.float32([1e6, -500.0])), "e4m3").tolist() == \
+        [448.0, -448.0]
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(3).standard_normal(20000).astype(np.float32) * 50
+    t = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(inputs.round_to_e4m3(x), t.numpy())
+
+
+def test_fp8_guide_example():
+    """Guide §5.3 row (scores 1, 3, 2, 4) stored in e4m3: q = e1, k_j = x_j e1, V = I; the
+    descales multiply to 1 on the scores (0.5 * 2) and scale V by 3."""
+    g = _golden("guide_online_softmax_example.json")
+    x = g["scores"]
+    n = len(x)
+    q = np.zeros((1, n, 1, n), dtype=np.float32)
+    q[0, 0, 0, 0] = 2.0                   # 2 * 0.5 = 1
+    k = np.zeros((1, n, 1, n), dtype=np.float32)
+    k[0, :, 0, 0] = np.asarray(x) / 2.0   # (x / 2) * 2 = x
+    v = np.eye(n, dtype=np.float32).reshape(1, n, 1, n)
+    qc, kc, vc = (inputs.round_to_e4m3(t) for t in (q, k, v))
+    o, lse = oracle.fwd_fp8(qc, kc, vc, 0.5, 2.0, 3.0, 1.0, False)
+    np.testing.assert_allclose(o[0, 0, 0] / 3.0, g["one_shot"]["softmax"], atol=g["abs_tol"])
+    assert math.exp(lse[0, 0, 0] - g["one_shot"]["max"]) == pytest.approx(
+        g["one_shot"]["sum"], abs=g["abs_tol"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_descales(causal):
+    """The value of a stored tensor is its descale times its codes' values: q_descale and
+    k_descale act as a factor on the scores, v_descale as a factor on the output."""
+    B, N, H, d = 1, 23, 2, 16
+    (qc, kc, vc), (qd, kd, _) = inputs.fp8_inputs(B, N, H, d, 5)
+    o1, l1 = oracle.fwd_fp8(qc, kc, vc, 1.0, 1.0, 1.0, 0.3 * 0.25 * 4.0, causal)
+    o2, l2 = oracle.fwd_fp8(qc, kc, vc, 0.25, 4.0, 1.0, 0.3, causal)
+    o3, l3 = oracle.fwd_fp8(qc, kc, vc, 0.25, 4.0, 0.125, 0.3, causal)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o3, 0.125 * o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l3, l1, rtol=0, atol=1e-12)
+    # a descale on q alone changes the scores (not a no-op)
+    o4, _ = oracle.fwd_fp8(qc, kc, vc, 2 * qd, kd, 1.0, 0.3, causal)
+    o5, _ = oracle.fwd_fp8(qc, kc, vc, qd, kd, 1.0, 0.3, causal)
+    assert np.abs(o4 - o5).max() > 1e-1
+
+
+def test_fp8_inputs_recipe():
+    """descale = amax / 448 per tensor, so the largest stored magnitude is 448 exactly."""
+    (qc, kc, vc), ds = inputs.fp8_inputs(2, 64, 3, 32, 0)
+    for c, s, i in zip((qc, kc, vc), ds, range(3)):
+        x = np.random.default_rng(0 + i).standard_normal((2, 64, 3, 32), dtype=np.float32)
+        assert s == pytest.approx(float(np.abs(x).max()) / 448, rel=1e-6)
+        assert np.abs(oracle.widen(c, "e4m3")).max() == 448.0
+        assert np.abs(oracle.widen(c, "e4m3") * s - x).max() <= 2.0 ** -4 * np.abs(x).max()
+
+
+@pytest.mark.parametrize("scale", [0.05, 1.0, 6.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_error_bound_holds_for_rounded_weights(scale, causal):
+    """The FP8 tolerance (tests/fp8_bound.py) against a direct simulation of its premise:
+    every weight exp(s - max) scaled by 2^delta (delta >= 0, drawn per key), rounded to the
+    nearest e4m3 code, and the output taken as the weighted mean of the rounded weights.
+    The bound must hold everywhere and must not be vacuous."""
+    from fp8_bound import fp8_bounds
+    N, d = 96, 16
+    rng = np.random.default_rng(11)
+    (qc, kc, vc), (qd, kd, vd) = inputs.fp8_inputs(1, N, 1, d, 9)
+    q, k, v = (oracle.widen(c, "e4m3")[0, :, 0, :] * s for c, s in zip((qc, kc, vc),
+                                                                        (qd, kd, vd)))
+    o, lse = oracle.fwd(q[None, :, None, :], k[None, :, None, :], v[None, :, None, :], scale,
+                        causal)
+    o, lse = o[0, :, 0, :], lse[0, 0]
+    ob, lb = fp8_bounds(q, k, v, o, scale, causal)
+    worst = 0.0
+    for trial in range(4):
+        s = scale * q @ k.T
+        if causal:
+            s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        delta = rng.uniform(0.0, 8.0, size=p.shape) * (trial > 0)
+        big = (p * np.exp2(delta)).astype(np.float32)
+        pr = oracle.widen(inputs.round_to_e4m3(big), "e4m3") / np.exp2(delta)
+        o_sim = (pr @ v) / pr.sum(axis=1, keepdims=True)
+        lse_sim = np.log(pr.sum(axis=1)) + m[:, 0]
+        assert np.all(np.abs(o_sim - o) <= ob)
+        assert np.all(np.abs(lse_sim - lse) <= lb)
+        worst = max(worst, float((np.abs(o_sim - o) / ob).max()))
+    print(f"worst error/bound {worst:.3f}")
+    assert worst > 0.02, worst
