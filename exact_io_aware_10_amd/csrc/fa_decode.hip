@@ -43,23 +43,6 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag behind
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// 16 bytes per lane from a buffer into LDS: lane l writes lds_addr + OFF + 16 l with the
-// bytes at voff + OFF (zeros past the buffer's size). lds_addr is wave-uniform (M0).
-template <int OFF>
-__device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff) {
-  static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen offset:%3 lds"
-               :
-               : "{m0}"(lds_addr), "v"(voff), "s"(rs), "i"(OFF)
-               : "memory");
-}
-// Wait until at most N vector-memory operations of this wave are outstanding. Written in
-// assembly with a memory clobber so that no LDS read moves above it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 // acc + pair[0] + pair[1] for a packed pair of the element type, with the pair (1, 1) held in
 // a register. The pair is taken by value: a bit cast applied directly to a vector element
 // expression compiled to a cast of element 0.
@@ -71,10 +54,6 @@ __device__ __forceinline__ float add_pair_ones(uint32_t pair, uint32_t ones, flo
   else
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair),
                                   __builtin_bit_cast(f16x2, ones), acc, false);
-}
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t nbytes) {
-  const uint64_t a = (uint64_t)base;
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, nbytes, 0x00020000u};
 }
 
 template <int D, class T, bool CAUSAL>

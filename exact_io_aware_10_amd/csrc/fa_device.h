@@ -123,6 +123,33 @@ __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t of
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
 
+// Direct buffer -> LDS loads written in inline assembly. The builtin form tells the compiler
+// that the instruction writes LDS, so it makes every later LDS read wait for the load to
+// land (a wait on the HBM round trip). In assembly the load is opaque to the compiler: the
+// caller waits explicitly (wait_vmcnt) before any wave reads the data.
+// Words of a buffer resource over [base, base + nbytes), as make_rsrc.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, nbytes, 0x00020000u};
+}
+// 16 bytes per lane from a buffer into LDS: lane l writes lds_addr + OFF + 16 l with the
+// bytes at voff + OFF (zeros past the buffer's size). lds_addr is wave-uniform (M0).
+template <int OFF>
+__device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff) {
+  static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen offset:%3 lds"
+               :
+               : "{m0}"(lds_addr), "v"(voff), "s"(rs), "i"(OFF)
+               : "memory");
+}
+// Wait until at most N vector-memory operations of this wave are outstanding. Written in
+// assembly with a memory clobber so that no LDS read moves above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Row reductions across the lane pair (l, l ^ 32). v_permlane32_swap exchanges the upper
 // half of its first operand with the lower half of its second; with both operands = x the
 // two results hold, per lane, x and the partner's x (in an order that depends on the half),

@@ -21,7 +21,11 @@
 //
 // Layout on the chip, as in the 16-bit kernel: 8 waves = 256 query rows per workgroup, the
 // two groups of four waves ping-pong between matrix and vector phases, 128-key tiles of K
-// and V (16 KiB each at d = 128) go HBM -> LDS with buffer_load ... lds, double buffered.
+// and V (16 KiB each at d = 128) go HBM -> LDS with buffer_load ... lds, double buffered,
+// issued by group A during its matrix phases. At these rates the vector phase (64 exp2 per
+// lane per tile at a quarter of the vector rate, plus the max, the exponent's FMA and the
+// conversions) is the longer one, so the kernel is bound by vector issue, not by the matrix
+// cores.
 //
 // Operand layouts (lane l, l32 = l % 32, g = l / 32). The 32x32x64 MFMA takes 32 bytes per
 // lane for A and for B; any assignment of (lane half, byte) to the contraction index that
@@ -47,7 +51,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -69,10 +72,34 @@ __device__ __forceinline__ f32x16 mfma_f8(u32x8 a, u32x8 b, f32x16 c) {
 }
 
 // Four fp32 values -> four e4m3 codes in one dword (byte 0 = x0), round to nearest even.
+// Each conversion writes one 16-bit half and keeps the other; the first one's kept half is
+// overwritten by the second, so it starts from x0's own bits rather than a zeroed register.
 __device__ __forceinline__ uint32_t pack4_e4m3(float x0, float x1, float x2, float x3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __builtin_bit_cast(int, x0), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
   return (uint32_t)w;
+}
+
+// Maximum of N values by three-input maxima (v_max3_f32): 64 -> 22 -> 8
+// -> 3 -> 1 in 31 instructions, four levels deep.
+template <int N>
+__device__ __forceinline__ float max_tree3(const float (&x)[N]) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else {
+    constexpr int M = (N + 2) / 3;
+    float y[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if (3 * i + 2 < N)
+        y[i] = fmaxf(fmaxf(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+      else if (3 * i + 1 < N)
+        y[i] = fmaxf(x[3 * i], x[3 * i + 1]);
+      else
+        y[i] = x[3 * i];
+    }
+    return max_tree3<M>(y);
+  }
 }
 
 // 16-byte chunk swizzle of tile row r: logical chunk c is stored at c ^ swz(r). LDS serves
@@ -88,6 +115,39 @@ __device__ __forceinline__ int swz(int r) {
     return 2 * (((r >> 1) & 3) ^ ((r >> 2) & 2));
   else  // 64-byte rows, 4 chunks: rows r, r+4, r+8, r+12 share banks
     return (2 * ((r >> 3) & 1)) ^ ((r >> 2) & 1);
+}
+
+#ifndef FA_FP8_PREFETCH
+#define FA_FP8_PREFETCH 3  // MFMAs of look-ahead for the LDS operand reads (0: compiler order)
+#endif
+
+// Instruction order of one matrix phase: per 64-key half, DB MFMAs of O += P V (four
+// transposed reads each) and the row-sum MFMA (no reads), then the score MFMAs (two reads
+// each). Each MFMA's reads are issued PD MFMAs ahead, so their latency is covered by the
+// wave's own matrix work; the other wave on the SIMD is in its vector phase.
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+template <int DB>
+constexpr int xreads(int m) { return m < kKH * (DB + 1) ? (m % (DB + 1) < DB ? 4 : 0) : 2; }
+template <int DB>
+constexpr int xreads_before(int n) {
+  int r = 0;
+  for (int m = 0; m < n; ++m) r += xreads<DB>(m);
+  return r;
+}
+template <int DB, int NM, int PD, int M>
+__device__ __forceinline__ void xsched_step() {
+  sched_group<kSchedMfma, 1>();
+  if constexpr (M + PD < NM) sched_group<kSchedDsRead, xreads<DB>(M + PD)>();
+}
+template <int DB, int PD, int... M>
+__device__ __forceinline__ void xsched(std::integer_sequence<int, M...>) {
+  constexpr int NM = sizeof...(M);
+  sched_group<kSchedDsRead, xreads_before<DB>(PD < NM ? PD : NM)>();
+  (xsched_step<DB, NM, PD, M>(), ...);
 }
 
 template <int D, bool CAUSAL>
@@ -131,8 +191,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   const long base = (tok0 * a.H + h) * D;
   const uint32_t nbytes = (uint32_t)(L - 1) * rstride + D;
   const auto rq = make_rsrc(a.q + base, nbytes);
-  const auto rk = make_rsrc(a.k + base, nbytes);
-  const auto rv = make_rsrc(a.v + base, nbytes);
   const auto ro = make_rsrc(a.o + base, 2 * nbytes);  // bf16 output: twice the byte offsets
   float* lse = a.lse + ((long)bs * a.H + h) * a.N;
 
@@ -154,15 +212,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   // ---- direct HBM/L2 -> LDS tile loads: this wave fills LPW 1 KiB blocks of a tile; lane l
   // of a block writes row blk*RPL + l/CPR, physical chunk l%CPR.
   const int lrow = lane / CPR, lpc = lane % CPR;
-  auto tload = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* tile, int t) __attribute__((always_inline)) {
+  // The loads are issued from inline assembly (dma16): with the builtin the compiler would
+  // make the matrix phase's LDS reads wait for these loads to land.
+  const u32x4 wk = rsrc_words(a.k + base, nbytes), wv = rsrc_words(a.v + base, nbytes);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto tload = [&](bool is_k, uint8_t* tile, int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int blk = (wave & 3) * LPW + j;
       const int row = blk * RPL + lrow;
       const int c = lpc ^ swz<D>(row);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void*)(tile + blk * 1024), 16,
-          (uint32_t)(t * kBK + row) * rstride + c * 16, 0, 0, 0);
+      const uint32_t m0 =
+          __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(tile - smem) + blk * 1024);
+      dma16<0>(is_k ? wk : wv, m0, (uint32_t)(t * kBK + row) * rstride + c * 16);
     }
   };
 
@@ -233,6 +295,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
           s[kb] = mfma_f8(ka, qreg[dc], s[kb]);
         }
     }
+    if constexpr (decltype(HAS_PV)::value && decltype(HAS_S)::value && FA_FP8_PREFETCH > 0)
+      xsched<DB, FA_FP8_PREFETCH>(
+          std::make_integer_sequence<int, kKH * (DB + 1) + kKB * DC>{});
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       kcur[dc][0] ^= TILEB;
@@ -257,18 +322,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
           s[kb][r] = drop ? kNegInf : s[kb][r];
         }
     }
-    float m8[4 * kKB];
+    float sv[16 * kKB];
 #pragma unroll
-    for (int i = 0; i < 4 * kKB; ++i) {
-      const f32x16& x = s[i >> 2];
-      const int r = 4 * (i & 3);
-      m8[i] = fmaxf(fmaxf(x[r], x[r + 1]), fmaxf(x[r + 2], x[r + 3]));
-    }
-#pragma unroll
-    for (int w2 = 4 * kKB; w2 > 1; w2 >>= 1)
-#pragma unroll
-      for (int i = 0; i < w2 / 2; ++i) m8[i] = fmaxf(m8[2 * i], m8[2 * i + 1]);
-    const float mnew = pair_max(m8[0]) * c2;  // c2 > 0: a fully masked row keeps -inf
+    for (int i = 0; i < 16 * kKB; ++i) sv[i] = s[i >> 4][i & 15];
+    const float mnew = pair_max(max_tree3(sv)) * c2;  // c2 > 0: a fully masked row keeps -inf
     const bool need = mnew > mref + kRescaleSlack;
     if (__any(need)) {
       const float alpha = need ? exp2f_hw(mref - mnew) : 1.0f;
@@ -290,13 +347,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       }
   };
 
-  // Group B issues the direct loads at the start of its vector phase Y(t): K(t+2) into
-  // K buffer t % 2 and V(t+1) into V buffer (t+1) % 2, which both groups finished reading at
-  // the previous barrier.
-  auto loads = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 < ntiles) tload(rk, (t & 1) ? Ks1 : Ks0, t + 2);
-    if (t + 1 < ntiles) tload(rv, (t & 1) ? Vs0 : Vs1, t + 1);
-  };
   using I0 = std::integral_constant<bool, false>;
   using I1 = std::integral_constant<bool, true>;
   auto phase_barrier = [&]() __attribute__((always_inline)) {
@@ -313,47 +363,62 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 #pragma unroll
     for (int kh = 0; kh < kKH; ++kh) asm volatile("" : "+v"(pf[kh]));
   };
-  auto finish_x = [&]() __attribute__((always_inline)) {
-    if (grp == 1) __builtin_amdgcn_s_waitcnt(0);
-    phase_barrier();
+  // Group A issues the direct loads at the start of its matrix phase X(t): K(t+1) into K
+  // buffer (t+1) % 2 and V(t) into V buffer t % 2, buffers whose tiles every wave finished
+  // reading in X(t-1). It waits for them at the end of Y(t), before the barrier that precedes
+  // their first reader X(t+1). The vector phases, which set the pace, issue no loads (issued
+  // there, the loads lengthened them by a fifth).
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    if (grp == 0) {
+      if (t + 1 < ntiles) tload(true, ((t + 1) & 1) ? Ks1 : Ks0, t + 1);
+      if (t < ntiles) tload(false, (t & 1) ? Vs1 : Vs0, t);
+    }
+  };
+  auto land = [&]() __attribute__((always_inline)) {
+    if (grp == 0) wait_vmcnt<0>();
   };
   auto step = [&](int t) __attribute__((always_inline)) {
+    issue(t);
     xphase(I1{}, I1{});
     pin_s();
-    finish_x();
-    if (grp == 1) loads(t);
+    phase_barrier();
     yphase(t);
     pin_p();
+    land();
     phase_barrier();
   };
 
   // Phase p: group A runs X(p/2) for even p and Y(p/2) for odd p, group B one phase later.
-  if (grp == 1) tload(rk, Ks0, 0);
+  // A wave's own tiles end at nt_w; it then passes the remaining barriers idle (group A
+  // still issuing its share of the loads).
+  if (grp == 0) tload(true, Ks0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   phase_barrier();
-  if (grp == 1) {
-    if (ntiles > 1) tload(rk, Ks1, 1);
-    tload(rv, Vs0, 0);
-    phase_barrier();
-  }
+  if (grp == 1) phase_barrier();
+  issue(0);
   xphase(I0{}, I1{});
   pin_s();
-  finish_x();
-  if (grp == 1) loads(0);
+  phase_barrier();
   yphase(0);
   pin_p();
+  land();
   phase_barrier();
   int t = 1;
 #pragma unroll 1
   for (; t < nt_w; ++t) step(t);
+  issue(t);
   xphase(I1{}, I0{});
-  finish_x();
+  phase_barrier();
   for (; t < ntiles; ++t) {
-    if (grp == 1) loads(t);
+    land();
     phase_barrier();
-    finish_x();
+    issue(t + 1);
+    phase_barrier();
   }
-  if (grp == 0) phase_barrier();
+  if (grp == 0) {
+    land();
+    phase_barrier();
+  }
 
   // ---- epilogue: O = v_descale * acc / l in bf16 (rows >= L dropped by the bounds), LSE
   const float l = lacc[0];
