@@ -163,6 +163,28 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Maximum of N values by three-input maxima (v_max3_f32 from fmaxf(fmaxf(a, b), c)): for
+// N = 64, 64 -> 22 -> 8 -> 3 -> 1 in 31 instructions, four levels deep.
+template <int N>
+__device__ __forceinline__ float max_tree3(const float (&x)[N]) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else {
+    constexpr int M = (N + 2) / 3;
+    float y[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if (3 * i + 2 < N)
+        y[i] = fmaxf(fmaxf(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+      else if (3 * i + 1 < N)
+        y[i] = fmaxf(x[3 * i], x[3 * i + 1]);
+      else
+        y[i] = x[3 * i];
+    }
+    return max_tree3<M>(y);
+  }
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (XCD = linear id % 8), each with
 // its own L2. Remap the linear id so that XCD x receives a contiguous range of logical
 // work items; neighbouring items (query blocks of one head) then share that XCD's L2.

@@ -15,7 +15,7 @@
 //    and a vector phase Y_t = [online softmax of S(t) -> P(t)], group B one phase behind
 //    group A, with a workgroup barrier between phases; so on every SIMD one wave issues
 //    matrix instructions while the other does the exp/max/convert work.
-//  - key/value tiles of 64 rows go from HBM/L2 straight into LDS (buffer_load ... lds,
+//  - key/value tiles of 128 rows go from HBM/L2 straight into LDS (buffer_load ... lds,
 //    bounds-checked so rows past the sequence read as zero), double buffered, issued by
 //    group B during its vector phases. Rows are stored unpadded with an XOR swizzle of
 //    their 16-byte chunks that keeps the operand reads conflict-free.
@@ -57,7 +57,6 @@ constexpr float kNegInf = -__builtin_inff();
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // 16-byte-chunk swizzles of a tile row r (D/8 chunks per row).
 // K rows are read as 32 rows x one chunk (ds_read_b128): chunk c of row r sits at c ^ (r % D/8).
@@ -148,8 +147,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const long base = (tok0 * a.H + h) * D;
   const uint32_t nbytes = (uint32_t)(L - 1) * rstride + D * 2;
   const auto rq = make_rsrc(a.q + base, nbytes);
-  const auto rk = make_rsrc(a.k + base, nbytes);
-  const auto rv = make_rsrc(a.v + base, nbytes);
   const auto ro = make_rsrc(a.o + base, nbytes);
   float* lse = a.lse + (VARLEN ? (long)h * a.T + tok0 : ((long)bs * a.H + h) * a.N);
 
@@ -165,17 +162,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     qreg[dc] = buf_load16(rq, (uint32_t)qi * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
 
   // ---- direct HBM/L2 -> LDS tile loads: this wave fills LPW 1 KiB blocks of each tile;
-  // lane l of a block writes row blk*RPL + l/CPR, physical chunk l%CPR.
+  // lane l of a block writes row blk*RPL + l/CPR, physical chunk l%CPR. Issued from inline
+  // assembly (dma16), so the compiler adds no wait of its own; the issuing waves wait
+  // (vmcnt 0) before the barrier that precedes the tile's first reader.
   const int lrow = lane / CPR, lpc = lane % CPR;
-  auto tload = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* tile, int t, bool is_k) __attribute__((always_inline)) {
+  const u32x4 wk = rsrc_words(a.k + base, nbytes), wv = rsrc_words(a.v + base, nbytes);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto tload = [&](bool is_k, uint8_t* tile, int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int blk = (wave & 3) * LPW + j;
       const int row = blk * RPL + lrow;
       const int c = lpc ^ (is_k ? kswz<D>(row) : vswz<D>(row));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void*)(tile + blk * 1024), 16,
-          (uint32_t)(t * kBK + row) * rstride + c * 16, 0, 0, 0);
+      const uint32_t m0 =
+          __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(tile - smem) + blk * 1024);
+      dma16<0>(is_k ? wk : wv, m0, (uint32_t)(t * kBK + row) * rstride + c * 16);
     }
   };
 
@@ -266,20 +267,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
           s[kb][r] = drop ? kNegInf : s[kb][r];
         }
     }
-    // Row max as a tree of independent maxima: one wave runs this phase alone on its SIMD,
-    // so the dependency depth, not the instruction count, sets the phase length.
-    float m8[4 * kKB];
+    // Row max as a tree of three-input maxima: one wave runs this phase alone on its SIMD, so
+    // the dependency depth, not only the instruction count, sets the phase length.
+    float sv[16 * kKB];
 #pragma unroll
-    for (int i = 0; i < 4 * kKB; ++i) {
-      const f32x16& x = s[i >> 2];
-      const int r = 4 * (i & 3);
-      m8[i] = fmaxf(fmaxf(x[r], x[r + 1]), fmaxf(x[r + 2], x[r + 3]));
-    }
-#pragma unroll
-    for (int w = 4 * kKB; w > 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w / 2; ++i) m8[i] = fmaxf(m8[2 * i], m8[2 * i + 1]);
-    const float mx = m8[0];
+    for (int i = 0; i < 16 * kKB; ++i) sv[i] = s[i >> 4][i & 15];
+    const float mx = max_tree3(sv);
     const float mnew = pair_max(mx) * c2;  // c2 > 0: a fully masked row keeps -inf
     const bool need = mnew > mref + kRescaleSlack;
     if (__any(need)) {
@@ -314,14 +307,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     lsum = ls[0];
   };
 
-  // Group B issues the direct loads at the start of its vector phase Y(t): K(t+2) into
-  // K buffer t % 2 and V(t+1) into V buffer (t+1) % 2, the buffers both groups finished reading at
-  // the previous barrier; they have landed (vmcnt 0 in the issuing waves) by the barrier
-  // that closes the next phase.
-  auto loads = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 < ntiles) tload(rk, (t & 1) ? Ks1 : Ks0, t + 2, true);
-    if (t + 1 < ntiles) tload(rv, (t & 1) ? Vs0 : Vs1, t + 1, false);
-  };
   using I0 = std::integral_constant<bool, false>;
   using I1 = std::integral_constant<bool, true>;
   // workgroup barrier between phases; the scheduling barriers keep each phase's
@@ -341,8 +326,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int kc = 0; kc < kKC; ++kc) asm volatile("" : "+v"(pf[kc]));
   };
+  // Group B issues the direct loads at the start of its vector phase Y(t): K(t+2) into
+  // K buffer t % 2 and V(t+1) into V buffer (t+1) % 2, the buffers both groups finished reading
+  // at the previous barrier; they have landed (vmcnt 0 in the issuing waves) by the barrier
+  // that closes the next phase. (Issued in group A's matrix phases instead, they lengthen
+  // those, which are the longer phases here: 4% slower.)
+  auto loads = [&](int t) __attribute__((always_inline)) {
+    if (t + 2 < ntiles) tload(true, (t & 1) ? Ks1 : Ks0, t + 2);
+    if (t + 1 < ntiles) tload(false, (t & 1) ? Vs0 : Vs1, t + 1);
+  };
   auto finish_x = [&]() __attribute__((always_inline)) {
-    if (grp == 1) __builtin_amdgcn_s_waitcnt(0);
+    if (grp == 1) wait_vmcnt<0>();
     phase_barrier();
   };
   // X(t) then Y(t), for 1 <= t < nt_w
@@ -358,12 +352,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 
   // Phase p: group A runs X(p/2) for even p and Y(p/2) for odd p, group B one phase later.
   // A wave's own tiles end at nt_w; it then passes the remaining barriers idle.
-  if (grp == 1) tload(rk, Ks0, 0, true);
-  __builtin_amdgcn_s_waitcnt(0);
+  if (grp == 1) tload(true, Ks0, 0);
+  wait_vmcnt<0>();
   phase_barrier();
   if (grp == 1) {
-    if (ntiles > 1) tload(rk, Ks1, 1, true);
-    tload(rv, Vs0, 0, false);
+    if (ntiles > 1) tload(true, Ks1, 1);
+    tload(false, Vs0, 0);
     phase_barrier();
   }
   xphase(I0{}, I1{});

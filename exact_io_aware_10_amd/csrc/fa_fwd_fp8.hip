@@ -80,28 +80,6 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float x0, float x1, float x2, flo
   return (uint32_t)w;
 }
 
-// Maximum of N values by three-input maxima (v_max3_f32): 64 -> 22 -> 8
-// -> 3 -> 1 in 31 instructions, four levels deep.
-template <int N>
-__device__ __forceinline__ float max_tree3(const float (&x)[N]) {
-  if constexpr (N == 1) {
-    return x[0];
-  } else {
-    constexpr int M = (N + 2) / 3;
-    float y[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      if (3 * i + 2 < N)
-        y[i] = fmaxf(fmaxf(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
-      else if (3 * i + 1 < N)
-        y[i] = fmaxf(x[3 * i], x[3 * i + 1]);
-      else
-        y[i] = x[3 * i];
-    }
-    return max_tree3<M>(y);
-  }
-}
-
 // 16-byte chunk swizzle of tile row r: logical chunk c is stored at c ^ swz(r). LDS serves
 // 256 bytes per cycle from 64 banks; a 16-byte read is served 8 lanes at a time and an
 // 8-byte read 16 or 32 lanes at a time. The swizzle keeps both operand reads conflict-free:
