@@ -72,16 +72,18 @@ struct Tile {
   static constexpr int LPW = BYTES / 1024 / NW;  // direct loads per wave per tile (NW waves)
 
   // direct HBM/L2 -> LDS load of tile rows [row0, row0 + kTile) of a [tokens, H, D] tensor
-  static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint8_t* tile,
-                                              int row0, uint32_t rstride, int wave, int lane) {
+  // (rs: the tensor's buffer resource words). Issued from inline assembly (dma16): with the
+  // builtin the compiler makes the next LDS reads of the current tile wait for this
+  // prefetch. The caller waits (vmcnt 0) before the barrier that precedes the tile's readers.
+  static __device__ __forceinline__ void load(u32x4 rs, uint8_t* tile, int row0,
+                                              uint32_t rstride, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int blk = wave * LPW + j;
       const int row = blk * RPL + lane / CPR;
       const int c = (lane % CPR) ^ swz<D>(row);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + blk * 1024), 16,
-                                               (uint32_t)(row0 + row) * rstride + c * 16, 0,
-                                               0, 0);
+      dma16<0>(rs, __builtin_amdgcn_readfirstlane(lds_addr(tile) + blk * 1024),
+               (uint32_t)(row0 + row) * rstride + c * 16);
     }
   }
 };

@@ -48,14 +48,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const uint32_t rstride = (uint32_t)a.H * D * 2;
   const long base = (si.tok0 * a.H + h) * D;
   const uint32_t nbytes = (uint32_t)(L - 1) * rstride + D * 2;
-  const auto rq = make_rsrc(a.q + base, nbytes);
+  const u32x4 rq = rsrc_words(a.q + base, nbytes);
   const auto rk = make_rsrc(a.k + base, nbytes);
-  const auto rv = make_rsrc(a.v + base, nbytes);
-  const auto rdo = make_rsrc(a.dout + base, nbytes);
+  const u32x4 rv = rsrc_words(a.v + base, nbytes);
+  const u32x4 rdo = rsrc_words(a.dout + base, nbytes);
   const auto rdk = make_rsrc(a.dk + base, nbytes);
   const auto rdv = make_rsrc(a.dv + base, nbytes);
-  const auto rnl = make_rsrc(a.neg_lse2 + si.stat, (uint32_t)L * 4);
-  const auto rnd = make_rsrc(a.neg_delta + si.stat, (uint32_t)L * 4);
+  const u32x4 rnl = rsrc_words(a.neg_lse2 + si.stat, (uint32_t)L * 4);
+  const u32x4 rnd = rsrc_words(a.neg_delta + si.stat, (uint32_t)L * 4);
 
   const int wk0 = k0 + kg * 32;  // this wave's keys: wk0 .. wk0+31
   const int key = wk0 + l32;     // the key this lane's accumulators belong to
@@ -83,10 +83,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     TL::load(rq, qs, qt * kTile, rstride, wave, lane);
     TL::load(rdo, dos, qt * kTile, rstride, wave, lane);
     if (wave == 0) {  // 64 lanes x 4 bytes: one row term per query of the tile
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rnl, (lds_void*)nl, 4, (qt * kTile + lane) * 4,
-                                               0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rnd, (lds_void*)nd, 4, (qt * kTile + lane) * 4,
-                                               0, 0, 0);
+      dma4<0>(rnl, __builtin_amdgcn_readfirstlane(lds_addr(nl)), (qt * kTile + lane) * 4);
+      dma4<0>(rnd, __builtin_amdgcn_readfirstlane(lds_addr(nd)), (qt * kTile + lane) * 4);
     }
   };
 

@@ -40,8 +40,8 @@ __global__ __launch_bounds__(kThreads, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdArgs
   const long base = (si.tok0 * a.H + h) * D;
   const uint32_t nbytes = (uint32_t)(L - 1) * rstride + D * 2;
   const auto rq = make_rsrc(a.q + base, nbytes);
-  const auto rk = make_rsrc(a.k + base, nbytes);
-  const auto rv = make_rsrc(a.v + base, nbytes);
+  const u32x4 rk = rsrc_words(a.k + base, nbytes);
+  const u32x4 rv = rsrc_words(a.v + base, nbytes);
   const auto rdo = make_rsrc(a.dout + base, nbytes);
   const auto rdq = make_rsrc(a.dq + base, nbytes);
 

@@ -142,6 +142,19 @@ __device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff
                : "{m0}"(lds_addr), "v"(voff), "s"(rs), "i"(OFF)
                : "memory");
 }
+// 4 bytes per lane from a buffer into LDS: lane l writes lds_addr + OFF + 4 l.
+template <int OFF>
+__device__ __forceinline__ void dma4(u32x4 rs, uint32_t lds_addr, uint32_t voff) {
+  static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+  asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen offset:%3 lds"
+               :
+               : "{m0}"(lds_addr), "v"(voff), "s"(rs), "i"(OFF)
+               : "memory");
+}
+// LDS byte address of a pointer into a __shared__ array (the value M0 takes).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
 // Wait until at most N vector-memory operations of this wave are outstanding. Written in
 // assembly with a memory clobber so that no LDS read moves above it.
 template <int N>
