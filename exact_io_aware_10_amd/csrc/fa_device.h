@@ -142,6 +142,17 @@ __device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff
                : "{m0}"(lds_addr), "v"(voff), "s"(rs), "i"(OFF)
                : "memory");
 }
+// As dma16, with a wave-uniform byte offset soff added to every lane's voff (the
+// instruction's scalar offset): loads that differ only by a uniform amount share voff.
+template <int OFF>
+__device__ __forceinline__ void dma16s(u32x4 rs, uint32_t lds_addr, uint32_t voff,
+                                       uint32_t soff) {
+  static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds"
+               :
+               : "{m0}"(lds_addr), "v"(voff), "s"(rs), "s"(soff), "i"(OFF)
+               : "memory");
+}
 // 4 bytes per lane from a buffer into LDS: lane l writes lds_addr + OFF + 4 l.
 template <int OFF>
 __device__ __forceinline__ void dma4(u32x4 rs, uint32_t lds_addr, uint32_t voff) {
@@ -161,6 +172,16 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier between phases that share LDS: waits for this wave's LDS accesses
+// (lgkmcnt) but not for its outstanding buffer -> LDS loads. __syncthreads() would also wait
+// for those (vmcnt 0), i.e. for every prefetch meant to stay in flight across the barrier;
+// the kernels wait for each prefetch explicitly (wait_vmcnt) before the barrier that
+// precedes its readers. The memory clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Row reductions across the lane pair (l, l ^ 32). v_permlane32_swap exchanges the upper

@@ -168,16 +168,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const int lrow = lane / CPR, lpc = lane % CPR;
   const u32x4 wk = rsrc_words(a.k + base, nbytes), wv = rsrc_words(a.v + base, nbytes);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  // Per-lane part of each load's source offset: the lane's row within its 1 KiB block and its
+  // swizzled chunk (computed once); the block's first row and the tile are a uniform offset
+  // passed as the instruction's scalar offset, so issuing a load takes no vector work.
+  uint32_t kof[LPW], vof[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int row = ((wave & 3) * LPW + j) * RPL + lrow;
+    kof[j] = (uint32_t)lrow * rstride + (uint32_t)((lpc ^ kswz<D>(row)) * 16);
+    vof[j] = (uint32_t)lrow * rstride + (uint32_t)((lpc ^ vswz<D>(row)) * 16);
+  }
+  auto tload_one = [&](bool is_k, uint8_t* tile, int t, int j) __attribute__((always_inline)) {
+    const int blk = (wave & 3) * LPW + j;
+    const uint32_t m0 =
+        __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(tile - smem) + blk * 1024);
+    dma16s<0>(is_k ? wk : wv, m0, is_k ? kof[j] : vof[j],
+              (uint32_t)(t * kBK + blk * RPL) * rstride);
+  };
   auto tload = [&](bool is_k, uint8_t* tile, int t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int blk = (wave & 3) * LPW + j;
-      const int row = blk * RPL + lrow;
-      const int c = lpc ^ (is_k ? kswz<D>(row) : vswz<D>(row));
-      const uint32_t m0 =
-          __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(tile - smem) + blk * 1024);
-      dma16<0>(is_k ? wk : wv, m0, (uint32_t)(t * kBK + row) * rstride + c * 16);
-    }
+    for (int j = 0; j < LPW; ++j) tload_one(is_k, tile, t, j);
   };
 
   // ---- per-lane LDS byte offsets of the MFMA operand reads, relative to a tile buffer.
@@ -313,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // instructions on their side of it
   auto phase_barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
   // Results a phase hands to the next one are pinned on its side of the barrier: without

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   using I1 = std::integral_constant<bool, true>;
   auto phase_barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
   // results a phase hands to the next are pinned on its side of the barrier
