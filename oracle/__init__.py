@@ -44,8 +44,10 @@ def _load():
         lib.oracle_fwd_decode_split.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, D, I, L, I]
         lib.oracle_bwd_varlen.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ip, L, L, L, L,
                                           D, I, I]
+        lib.oracle_merge.argtypes = [dp, dp, dp, dp, L, L, L, I]
         for f in ("oracle_fwd", "oracle_fwd_blocked", "oracle_bwd", "oracle_fwd_varlen",
-                  "oracle_bwd_varlen", "oracle_fwd_decode", "oracle_fwd_decode_split"):
+                  "oracle_bwd_varlen", "oracle_fwd_decode", "oracle_fwd_decode_split",
+                  "oracle_merge"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -181,6 +183,25 @@ def fwd_decode_split(q, k, v, scale, causal, nsplit, nthreads=None):
                                          nthreads or default_threads())
     _check(rc, "oracle_fwd_decode_split")
     return o, lse
+
+
+def merge(o_parts, lse_parts, nthreads=None):
+    """Merge partial results over disjoint key sets of the same query rows (the block-merge
+    rule with m_s = LSE_s, l_s = 1). o_parts: fp64 [P, B, N, H, d]; lse_parts: [P, B, H, N].
+    Returns (O [B, N, H, d], LSE [B, H, N])."""
+    o_parts = _f64(o_parts)
+    lse_parts = _f64(lse_parts)
+    P, B, N, H, d = o_parts.shape
+    assert lse_parts.shape == (P, B, H, N)
+    rows = B * N * H
+    op = np.ascontiguousarray(o_parts.reshape(P, rows, d))
+    lp = np.ascontiguousarray(lse_parts.transpose(0, 1, 3, 2).reshape(P, rows))
+    o = np.empty((rows, d))
+    lse = np.empty(rows)
+    rc = _load().oracle_merge(_p(op), _p(lp), _p(o), _p(lse), P, rows, d,
+                              nthreads or default_threads())
+    _check(rc, "oracle_merge")
+    return o.reshape(B, N, H, d), np.ascontiguousarray(lse.reshape(B, N, H).transpose(0, 2, 1))
 
 
 def _cu(cu_seqlens):

@@ -468,4 +468,25 @@ int oracle_fwd_decode_split(const double* q, const double* k, const double* v, d
   return 0;
 }
 
+// Merge of partial results given as (O_s, LSE_s): part s holds the normalised output and
+// the log-sum-exp of the same rows over its own disjoint set of keys (for instance one K/V
+// shard of a ring of devices). In the block-merge rule's terms a part has m_s = LSE_s and
+// l_s = 1 (l_s = 0 for a part that saw no key, LSE_s = -inf), so the merge is exactly
+// merge_partials. Layout: o_parts [nparts][rows][d], lse_parts [nparts][rows]; o [rows][d],
+// lse [rows]. Returns 0, or -1 on bad sizes.
+int oracle_merge(const double* o_parts, const double* lse_parts, double* o, double* lse,
+                 long nparts, long rows, long d, int nthreads) {
+  if (nparts < 1 || rows < 0 || d < 1) return -1;
+  parallel_for(rows, nthreads, [&](long r) {
+    std::vector<double> ms(nparts), ls(nparts), os(nparts * d);
+    for (long t = 0; t < nparts; ++t) {
+      ms[t] = lse_parts[t * rows + r];
+      ls[t] = ms[t] == kNegInf ? 0.0 : 1.0;
+      for (long c = 0; c < d; ++c) os[t * d + c] = o_parts[(t * rows + r) * d + c];
+    }
+    merge_partials(nparts, d, ms.data(), ls.data(), os.data(), o + r * d, lse[r]);
+  });
+  return 0;
+}
+
 }  // extern "C"

@@ -555,3 +555,57 @@ def test_fp8_error_bound_holds_for_rounded_weights(scale, causal):
         worst = max(worst, float((np.abs(o_sim - o) / ob).max()))
     print(f"worst error/bound {worst:.3f}")
     assert worst > 0.02, worst
+
+
+# ---------------------------------------------------------------- merging partial results (O, LSE)
+
+def test_merge_narration_example():
+    """The narration's row (exponentiated scores 1, 2 | 4, 3, values 10, 20 | 30, 40) as two
+    parts, each normalised over its own keys: merged O = 29 and LSE = ln 10 as printed."""
+    g = _golden("narration_online_softmax_example.json")
+    o1, l1 = (1 * 10 + 2 * 20) / 3, math.log(3)
+    o2, l2 = (4 * 30 + 3 * 40) / 7, math.log(7)
+    o, lse = oracle.merge(np.array([o1, o2]).reshape(2, 1, 1, 1, 1),
+                          np.array([l1, l2]).reshape(2, 1, 1, 1))
+    assert o[0, 0, 0, 0] == pytest.approx(g["output"], abs=1e-12)
+    assert lse[0, 0, 0] == pytest.approx(math.log(g["one_shot"]["weight_total"]), abs=1e-12)
+
+
+@pytest.mark.parametrize("parts", [2, 3, 5])
+def test_merge_of_key_shards_is_the_whole(parts):
+    """Attention of the same queries over disjoint key shards, merged, equals attention over
+    all keys (the rule is exact in real arithmetic)."""
+    B, N, H, d = 2, 30, 2, 8
+    q = _rand((B, N, H, d), 40)
+    k = _rand((B, N, H, d), 41)
+    v = _rand((B, N, H, d), 42)
+    ro, rl = oracle.fwd_decode(q, k, v, 0.4, False)
+    cuts = np.linspace(0, N, parts + 1).astype(int)
+    os, ls = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o, l = oracle.fwd_decode(q, k[:, a:b], v[:, a:b], 0.4, False)
+        os.append(o)
+        ls.append(l)
+    o, lse = oracle.merge(np.stack(os), np.stack(ls))
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+def test_merge_empty_parts():
+    """A part that saw no key (LSE = -inf) contributes nothing; all parts empty gives O = 0,
+    LSE = -inf; the order of the parts does not matter."""
+    o1 = _rand((1, 3, 1, 4), 50)
+    l1 = _rand((1, 1, 3), 51)
+    junk = _rand((1, 3, 1, 4), 52) * 100
+    ninf = np.full((1, 1, 3), -np.inf)
+    o, lse = oracle.merge(np.stack([o1, junk]), np.stack([l1, ninf]))
+    np.testing.assert_allclose(o, o1, atol=1e-15)
+    np.testing.assert_allclose(lse, l1, atol=1e-15)
+    o, lse = oracle.merge(np.stack([junk, junk]), np.stack([ninf, ninf]))
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    o2 = _rand((1, 3, 1, 4), 53)
+    l2 = _rand((1, 1, 3), 54)
+    a = oracle.merge(np.stack([o1, o2]), np.stack([l1, l2]))
+    b = oracle.merge(np.stack([o2, o1]), np.stack([l2, l1]))
+    np.testing.assert_allclose(a[0], b[0], atol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-14)
