@@ -10,6 +10,7 @@ current HIP stream. There is no fallback: if the library is missing the calls ra
     o, lse = fa_fwd_splitkv(q, k, v, causal=False, softmax_scale=None, num_splits=0)
     o, lse = fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False,
                         softmax_scale=None)
+    fa_merge(o_acc, lse_acc, o_part, lse_part, out=None)
 
 q, k, v, o, dout: [B, N, H, d] (packed: [T, H, d]) contiguous bf16 or fp16 CUDA tensors;
 lse: fp32 [B, H, N] (packed: [H, T]); d in {64, 128}; softmax_scale defaults to 1/sqrt(d).
@@ -22,6 +23,7 @@ import os
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen",
            "fa_bwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_fp8",
+           "fa_merge",
            "fa_bwd_workspace_size", "fa_status_string", "FAError", "library_path",
            "load_library"]
 
@@ -69,6 +71,8 @@ def load_library():
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_fp8.argtypes = [vp] * 5 + [i, i, i, i, f, f, f, f, i, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_merge.argtypes = [vp] * 5 + [i, i, i, i, i, vp]
+    lib.fa_merge.restype = i
     _lib = lib
     return lib
 
@@ -161,6 +165,29 @@ def fa_fwd_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=Fals
     if rc != FA_OK:
         raise FAError("fa_fwd_fp8", rc)
     return o, lse
+
+
+def fa_merge(o_acc, lse_acc, o_part, lse_part, out=None):
+    """Merge (o_part, lse_part) into the running (o_acc fp32 [B,N,H,d], lse_acc fp32
+    [B,H,N]) in place; o_part is bf16/fp16. If out is given (same dtype as o_part) it also
+    receives the merged output rounded to that dtype. Returns out (or None)."""
+    torch = _torch()
+    lib = load_library()
+    if o_part.dim() != 4:
+        raise ValueError("o_part must be [B, N, H, d]")
+    B, N, H, d = o_part.shape
+    _check_tensor("o_part", o_part, o_part.shape, o_part.dtype, o_part.device)
+    _check_tensor("o_acc", o_acc, o_part.shape, torch.float32, o_part.device)
+    _check_tensor("lse_acc", lse_acc, (B, H, N), torch.float32, o_part.device)
+    _check_tensor("lse_part", lse_part, (B, H, N), torch.float32, o_part.device)
+    if out is not None:
+        _check_tensor("out", out, o_part.shape, o_part.dtype, o_part.device)
+    rc = lib.fa_merge(o_acc.data_ptr(), lse_acc.data_ptr(), o_part.data_ptr(),
+                      lse_part.data_ptr(), None if out is None else out.data_ptr(), B, N, H, d,
+                      _dtype_code(o_part), _stream(o_part.device))
+    if rc != FA_OK:
+        raise FAError("fa_merge", rc)
+    return out
 
 
 def _bwd_call(fn, q, k, v, o, lse, dout, causal, softmax_scale, workspace, grads):

@@ -111,6 +111,28 @@ FA_EXPORT fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void
   return to_status(fa::launch_fwd_fp8(a, d, causal != 0, stream));
 }
 
+FA_EXPORT fa_status fa_merge(float* o_acc, float* lse_acc, const void* o_part,
+                             const float* lse_part, void* out, int B, int N, int H, int d,
+                             fa_dtype dtype, hipStream_t stream) {
+  fa_status st = check_common(B, N, H, d, dtype, 1.0f);
+  if (st != FA_OK) return st;
+  if ((long)B * N * H == 0) return FA_OK;
+  if (!tensors_ok({o_acc, o_part}) || (out != nullptr && !aligned16(out)) ||
+      lse_acc == nullptr || lse_part == nullptr || ((uintptr_t)lse_acc & 3u) ||
+      ((uintptr_t)lse_part & 3u))
+    return FA_ERR_INVALID_ARG;
+  fa::MergeArgs a{};
+  a.o_acc = o_acc;
+  a.lse_acc = lse_acc;
+  a.o_part = static_cast<const uint16_t*>(o_part);
+  a.lse_part = lse_part;
+  a.out = static_cast<uint16_t*>(out);
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  return to_status(fa::launch_merge(a, d, dtype == FA_BF16, stream));
+}
+
 FA_EXPORT size_t fa_bwd_workspace_size(int B, int N, int H, int d) {
   if (B < 0 || N < 0 || H < 0 || (d != 64 && d != 128)) return 0;
   return (size_t)8 * B * H * N;

@@ -53,6 +53,18 @@ struct Fp8FwdArgs {
   float v_descale;
 };
 
+// One merge of a partial result into a running one (same rows, disjoint key sets).
+struct MergeArgs {
+  float* o_acc;            // fp32 [B, N, H, d], in/out
+  float* lse_acc;          // fp32 [B, H, N], in/out
+  const uint16_t* o_part;  // [B, N, H, d], element type
+  const float* lse_part;   // fp32 [B, H, N]
+  uint16_t* out;           // [B, N, H, d], element type, or null
+  int B, N, H;
+};
+__attribute__((visibility("hidden"))) hipError_t launch_merge(const MergeArgs& a, int d,
+                                                              bool bf16, hipStream_t stream);
+
 __attribute__((visibility("hidden"))) hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, int d,
                                                                 bool causal,
                                                                 hipStream_t stream);

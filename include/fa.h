@@ -94,6 +94,31 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
                      float softmax_scale, int causal, hipStream_t stream);
 
 /*
+ * Merge of a partial attention result into a running one: the per-device step of ring
+ * (context-parallel) attention, where each device keeps its query rows and attends them to
+ * one K/V shard per step ("FlashAttention 与算子融合", 代际演进 table and 工程实践: ring attention
+ * with FlashAttention as the compute core), combined with the block-merge rule of the same
+ * page (section FlashAttention 的两个关键). For the same query rows, (o_acc, lse_acc) hold the
+ * result over the keys seen so far and (o_part, lse_part) the result over a disjoint set of
+ * keys, e.g. fa_fwd on one shard. In place, per row:
+ *   lse_acc <- ln(e^lse_acc + e^lse_part)
+ *   o_acc   <- o_acc e^(lse_acc_old - lse_acc) + o_part e^(lse_part - lse_acc)
+ * A side whose lse is -inf (no visible key) contributes nothing, whatever its o values;
+ * both -inf gives o_acc = 0, lse_acc = -inf. Start a ring from lse_acc = -inf (o_acc's
+ * contents are then ignored).
+ *   o_acc    : in/out, fp32 [B, N, H, d], 16-byte aligned (kept in fp32 across merges)
+ *   lse_acc  : in/out, fp32 [B, H, N]
+ *   o_part   : in, [B, N, H, d], dtype
+ *   lse_part : in, fp32 [B, H, N]
+ *   out      : out, [B, N, H, d], dtype, or NULL: the merged output rounded to dtype
+ * dtype FA_BF16 or FA_F16, d 64 or 128, sizes and limits as fa_fwd. Deterministic. For the
+ * backward, fa_bwd on each shard with the merged o (rounded) and lse gives that shard's dK,
+ * dV and its share of dQ (the shares of dQ add up).
+ */
+fa_status fa_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part,
+                   void* out, int B, int N, int H, int d, fa_dtype dtype, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs: 8 * B * H * N (two fp32 row terms per query:
  * -D_i = -<dO_i, O_i> and -LSE_i * log2(e)). Linear in N: the backward never stores an
  * N x N matrix. Returns 0 for arguments fa_bwd would reject as sizes (negative sizes or a

@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_prep",
          "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen", "fa_bwd_varlen",
-         "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv", "fa_fwd_fp8"])
+         "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_merge"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -184,3 +184,19 @@ def test_fp8_argument_checks(lib):
     assert call(N=1 << 20, H=64, d=128) == 2
     assert call(B=0) == 0
     assert call(q=None, N=0) == 0
+
+
+def test_merge_argument_checks(lib):
+    def call(oa=FAKE, la=FAKE, op=FAKE, lp=FAKE, out=FAKE, B=1, N=8, H=1, d=64, dt=1):
+        return lib.fa_merge(oa, la, op, lp, out, B, N, H, d, dt, None)
+
+    assert call(oa=None) == 1
+    assert call(op=None) == 1
+    assert call(la=None) == 1
+    assert call(lp=FAKE + 2) == 1               # misaligned lse
+    assert call(out=FAKE + 8) == 1              # misaligned output
+    assert call(B=-1) == 1
+    assert call(dt=5) == 1
+    assert call(d=96) == 2
+    assert call(N=1 << 20, H=64, d=128) == 2
+    assert call(out=None, B=0) == 0             # empty: nothing to do

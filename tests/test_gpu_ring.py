@@ -1,0 +1,128 @@
+"""GPU parity of fa_merge, and of one device's share of ring attention emulated on one GPU:
+the query rows of chunk r attend to every K/V chunk s in turn (fa_fwd per chunk, causal on
+the diagonal chunk, chunks after r skipped under the mask), the partial results are merged
+with fa_merge, and the backward runs per chunk (fa_bwd with the merged O and LSE), the
+shares of dQ, dK and dV added up. Everything is compared with the fp64 oracle on the whole
+sequence. The passing of K/V between devices is not part of this (one GPU)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_io_aware_10_amd import inputs
+from parity import assert_close, to_device, f64_of
+
+pytestmark = pytest.mark.gpu
+
+
+def fa():
+    import exact_io_aware_10_amd as m
+    return m
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_merge_against_oracle(d, dtype):
+    import torch
+    B, N, H = 2, 75, 3
+    print(f"[merge] B={B} N={N} H={H} d={d} {dtype}", flush=True)
+    rng = np.random.default_rng(d)
+    acc = rng.standard_normal((B, N, H, d)).astype(np.float32)
+    lacc = rng.standard_normal((B, H, N)).astype(np.float32) * 3
+    part_bits = inputs.normal_bits((B, N, H, d), dtype, 7)
+    lpart = rng.standard_normal((B, H, N)).astype(np.float32) * 3
+    # rows where one side, or both, saw no key
+    lacc[0, 0, :5] = -np.inf
+    lpart[0, 1, 3:9] = -np.inf
+    lacc[1, 2, 10:12] = -np.inf
+    lpart[1, 2, 10:12] = -np.inf
+    acc[0, :5, 0, :] = np.nan  # ignored where lse_acc = -inf
+    oa = torch.from_numpy(acc.copy()).cuda()
+    la = torch.from_numpy(lacc.copy()).cuda()
+    op = to_device(part_bits, dtype)
+    lp = torch.from_numpy(lpart.copy()).cuda()
+    out = torch.empty_like(op)
+    fa().fa_merge(oa, la, op, lp, out=out)
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge(np.stack([acc.astype(np.float64), oracle.widen(part_bits, dtype)]),
+                          np.stack([lacc.astype(np.float64), lpart.astype(np.float64)]))
+    got_o = oa.cpu().numpy().astype(np.float64)
+    got_l = la.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(rl))
+    fin = ~np.isneginf(rl)
+    np.testing.assert_allclose(got_l[fin], rl[fin], rtol=0, atol=2e-6 * (1 + np.abs(rl[fin])).max())
+    assert np.all(np.isfinite(got_o))
+    np.testing.assert_allclose(got_o, ro, rtol=2e-6, atol=2e-6)
+    # the rounded copy: within half an ulp of the element type (2^-9 relative for bf16)
+    assert_close("out", f64_of(out, dtype), ro, max_abs=1e-6, mean_abs=1e-2, rel_fro=1e-2,
+                 rtol=2.0 ** -8)
+
+
+def ring(B, N, H, d, dtype, causal, P, seed, backward):
+    """One device's share of ring attention, for every device r, on one GPU."""
+    import torch
+    print(f"[ring] B={B} N={N} H={H} d={d} {dtype} causal={causal} P={P} seed={seed}",
+          flush=True)
+    bits = inputs.attention_inputs(B, N, H, d, dtype, seed, with_dout=True)
+    q, k, v, do = (to_device(x, dtype) for x in bits)
+    c = N // P
+    ch = lambda t, i: t[:, i * c:(i + 1) * c].contiguous()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    for r in range(P):
+        qr = ch(q, r)
+        o_acc = torch.zeros((B, c, H, d), dtype=torch.float32, device=q.device)
+        l_acc = torch.full((B, H, c), -math.inf, dtype=torch.float32, device=q.device)
+        out = torch.empty_like(qr)
+        for s in range(P):
+            if causal and s > r:
+                continue  # the chunk lies after every query row of chunk r
+            o_s, l_s = fa().fa_fwd(qr, ch(k, s), ch(v, s), causal=causal and s == r)
+            fa().fa_merge(o_acc, l_acc, o_s, l_s, out=out)
+        o[:, r * c:(r + 1) * c] = out
+        lse[:, :, r * c:(r + 1) * c] = l_acc
+    grads = None
+    if backward:
+        dq = torch.zeros((B, N, H, d), dtype=torch.float32, device=q.device)
+        dk = torch.zeros_like(dq)
+        dv = torch.zeros_like(dq)
+        for r in range(P):
+            orr = ch(o, r)
+            lr = lse[:, :, r * c:(r + 1) * c].contiguous()
+            for s in range(P):
+                if causal and s > r:
+                    continue
+                g = fa().fa_bwd(ch(q, r), ch(k, s), ch(v, s), orr, lr, ch(do, r),
+                                causal=causal and s == r)
+                dq[:, r * c:(r + 1) * c] += g[0].float()
+                dk[:, s * c:(s + 1) * c] += g[1].float()
+                dv[:, s * c:(s + 1) * c] += g[2].float()
+        grads = [t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+    torch.cuda.synchronize()
+    return bits, f64_of(o, dtype), lse.cpu().numpy().astype(np.float64), grads
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("P", [2, 4])
+def test_ring_forward(causal, P):
+    B, N, H, d, dtype = 1, 1024, 2, 128, "bf16"
+    bits, o, lse, _ = ring(B, N, H, d, dtype, causal, P, seed=P, backward=False)
+    w = [oracle.widen(x, dtype) for x in bits]
+    ro, rl = oracle.fwd(w[0], w[1], w[2], 1 / math.sqrt(d), causal)
+    assert_close("O", o, ro)
+    assert_close("LSE", lse, rl)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ring_backward(causal):
+    B, N, H, d, dtype, P = 1, 768, 2, 64, "bf16", 3
+    bits, o, lse, (dq, dk, dv) = ring(B, N, H, d, dtype, causal, P, seed=11, backward=True)
+    w = [oracle.widen(x, dtype) for x in bits]
+    scale = 1 / math.sqrt(d)
+    ro, rl = oracle.fwd(w[0], w[1], w[2], scale, causal)
+    assert_close("O", o, ro)
+    rq, rk, rv = oracle.bwd(w[0], w[1], w[2], ro, rl, w[3], scale, causal)
+    # each chunk's share is rounded to bf16 before the shares are added: up to P roundings
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv)):
+        assert_close(name, g, r, rtol=P * 2.0 ** -9)
