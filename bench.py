@@ -47,6 +47,7 @@ KERNEL_SOURCES = {  # the files whose text determines each kernel's code (build.
                       "fa_internal.h", "../build.py"],
     "fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_internal.h", "../build.py"],
     "fwd_fp8_kernel": ["fa_fwd_fp8.hip", "fa_device.h", "fa_internal.h", "../build.py"],
+    "merge_kernel": ["fa_merge.hip", "fa_device.h", "fa_internal.h", "../build.py"],
     "bwd_prep_kernel": ["fa_bwd.hip", "fa_bwd_common.h", "fa_device.h", "fa_internal.h",
                         "../build.py"],
     "bwd_dkdv_kernel": ["fa_bwd_dkdv.hip", "fa_bwd_common.h", "fa_device.h", "fa_internal.h",
@@ -387,6 +388,107 @@ def fp8_main(args):
     print(json.dumps(out), flush=True)
 
 
+RING = dict(name="ring_step_16k", B=1, H=16, d=128, chunk=16384, devices=8)
+
+
+def merge_bytes(B, N, H, d):
+    """Compulsory bytes of one fa_merge: o_acc read and written (fp32), o_part read and the
+    rounded output written (2 bytes), and per row lse_acc read and written, lse_part read."""
+    return B * N * H * (4.0 * d * 2 + 2.0 * d * 2 + 12.0)
+
+
+def ring_cpu_baseline(q, k, v, c, d, min_s=10.0):
+    """The fp64 oracle on a sample of the ring step: for one head after another (until at
+    least min_s seconds have passed, at most all of them), the forward of the chunk against
+    one K/V chunk, then the merge into a running result."""
+    import oracle
+    nth = oracle.default_threads()
+    H = q.shape[2]
+    secs, heads = 0.0, 0
+    while heads < H and (heads == 0 or secs < min_s):
+        w = [oracle.widen(np.ascontiguousarray(x[:, :, heads:heads + 1, :]), "bf16")
+             for x in (q, k, v)]
+        t0 = time.perf_counter()
+        o, lse = oracle.fwd(w[0], w[1], w[2], 1 / math.sqrt(d), False, nthreads=nth)
+        oracle.merge(np.stack([o, o]), np.stack([lse, lse]), nthreads=nth)
+        secs += time.perf_counter() - t0
+        heads += 1
+    return {"value": round(heads * fwd_flops(1, c, 1, d, False) / secs / 1e12, 6),
+            "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
+            "sample": f"fp64 oracle forward + merge of {heads} of the {H} heads of one ring "
+                      f"step (chunk {c}, d={d}), {secs:.1f} s on {nth} host threads"}
+
+
+def ring_main(args):
+    """One JSON line for one device's step of ring attention: fa_fwd of the local query chunk
+    against one K/V chunk, then fa_merge into the running fp32 result. Both timed with HIP
+    events on their stream."""
+    import torch
+    import exact_io_aware_10_amd as fa
+    from exact_io_aware_10_amd import inputs
+
+    r = RING
+    B, H, d, c = r["B"], r["H"], r["d"], r["chunk"]
+    bits = inputs.attention_inputs(B, c, H, d, "bf16", 0)
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in bits)
+    o_s = torch.empty_like(q)
+    l_s = torch.empty((B, H, c), dtype=torch.float32, device="cuda")
+    o_acc = torch.zeros((B, c, H, d), dtype=torch.float32, device="cuda")
+    l_acc = torch.full((B, H, c), -math.inf, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fa.fa_fwd(q, k, v, out=o_s, lse=l_s)
+        if ev:
+            ev[1].record()
+        fa.fa_merge(o_acc, l_acc, o_s, l_s, out=out)
+        if ev:
+            ev[2].record()
+
+    for _ in range(max(args.warmup, 5)):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    f_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    m_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+    ff = fwd_flops(B, c, H, d, False)
+    mb = merge_bytes(B, c, H, d)
+    out_line = {
+        "metric": f"ring-attention step TFLOP/s, one device: chunk {c} of a "
+                  f"{c * r['devices']}-token ring of {r['devices']}, B{B} H{H} d{d} bf16",
+        "value": round(ff / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": max(args.warmup, 5), "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": r["name"], "B": B, "H": H, "d": d, "chunk": c,
+                   "devices": r["devices"], "causal": False,
+                   "step": "fa_fwd (chunk x chunk) + fa_merge"},
+        "fwd_ms": round(f_ms, 4), "merge_ms": round(m_ms, 4),
+        "merge_roofline": {"bound": "hbm", "kernel": "merge_kernel",
+                           "achieved": round(mb / (m_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": round(mb / (m_ms * 1e-3) / 1e9 /
+                                                         PEAK_HBM_GBPS, 4),
+                           "traffic": measured_traffic_for(f"merge_kernel_{r['name']}",
+                                                           "merge_kernel"),
+                           "bytes_per_launch": mb, "avg_launch_ms": round(m_ms, 4)},
+        "roofline": {"bound": "mfma", "kernel": "fwd_kernel",
+                     "achieved": round(ff / (f_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ff / (f_ms * 1e-3) / 1e12 /
+                                                      PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic_for(f"fwd_kernel_{r['name']}", "fwd_kernel"),
+                     "avg_launch_ms": round(f_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out_line["cpu_baseline"] = ring_cpu_baseline(*bits, c, d)
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     if "--rocprof-summary" in sys.argv:
         rocprof_summary(sys.argv[sys.argv.index("--rocprof-summary") + 1:])
@@ -404,8 +506,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--workload", default=WORKLOAD["name"],
                     help="long_seq_fwd_bwd (default), a decode workload (decode_8k, "
-                         "decode_128k) or an FP8 forward workload (long_seq_fp8, "
-                         "long_seq_causal_fp8)")
+                         "decode_128k), an FP8 forward workload (long_seq_fp8, "
+                         "long_seq_causal_fp8) or one device's ring-attention step "
+                         "(ring_step_16k)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -421,6 +524,9 @@ def main():
         copy_calibration(args.copy_calibration)
     if args.workload in inputs.FP8_WORKLOADS:
         fp8_main(args)
+        return
+    if args.workload == RING["name"]:
+        ring_main(args)
         return
     if args.workload != WORKLOAD["name"]:
         decode_main(args)
