@@ -16,9 +16,9 @@
 //    group A, with a workgroup barrier between phases; so on every SIMD one wave issues
 //    matrix instructions while the other does the exp/max/convert work.
 //  - key/value tiles of 128 rows go from HBM/L2 straight into LDS (buffer_load ... lds,
-//    bounds-checked so rows past the sequence read as zero), double buffered, issued by
-//    group B during its vector phases. Rows are stored unpadded with an XOR swizzle of
-//    their 16-byte chunks that keeps the operand reads conflict-free.
+//    bounds-checked so rows past the sequence read as zero), K triple and V double buffered,
+//    each group issuing one tile per step in its vector phase. Rows are stored unpadded with
+//    an XOR swizzle of their 16-byte chunks that keeps the operand reads conflict-free.
 //  - scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: each lane then
 //    holds 32 scores of ONE query row (the other 32 sit in lane l^32), so row max and row
 //    sum need only per-lane work plus one v_permlane32_swap.
@@ -103,13 +103,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   constexpr int DC = D / 16;                  // 16-wide d chunks of Q K^T
   constexpr int DB = D / 32;                  // 32-wide d blocks of the output
 
-  // four tile buffers: K at 0 and TILEB, V at 2 TILEB and 3 TILEB. A buffer's parity is bit
-  // log2(TILEB) of its offset, so switching buffers is an XOR of the per-lane offsets.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];
-  uint8_t* const Ks0 = smem;
-  uint8_t* const Ks1 = smem + TILEB;
-  uint8_t* const Vs0 = smem + 2 * TILEB;
-  uint8_t* const Vs1 = smem + 3 * TILEB;
+  // five tile buffers: V at 0 and TILEB (a V buffer's parity is bit log2(TILEB) of its
+  // offset, so switching V buffers is an XOR of the per-lane offsets), K at 2, 3 and 4 TILEB
+  // (three, so that a K tile can be loaded while both groups are still reading the two
+  // before it). 160 KiB at d = 128.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * TILEB];
+  auto kbuf = [&](int i) __attribute__((always_inline)) { return smem + (2 + i) * TILEB; };
+  auto vbuf = [&](int i) __attribute__((always_inline)) { return smem + i * TILEB; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
@@ -196,10 +196,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // K (A operand of S^T): row kb*32 + l32, logical chunk 2dc + g, stored at (2dc + g) ^ m,
   // m = l32 % (D/8); bit 0 comes from g alone, so this is 2(dc ^ m/2) + (g ^ m%2).
   const int km = kswz<D>(l32);
-  int kcur[DC];  // offsets into the K buffer of the current tile (starts at K buffer 0)
+  int kcur[DC];  // offsets of the current tile's K buffer (starts at K buffer 0)
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc)
-    kcur[dc] = l32 * ROWB + (2 * (dc ^ (km >> 1)) + (g ^ (km & 1))) * 16;
+    kcur[dc] = 2 * TILEB + l32 * ROWB + (2 * (dc ^ (km >> 1)) + (g ^ (km & 1))) * 16;
+  int kslot = 0;  // K buffer of the current tile (uniform)
   // V^T (A operand of O^T): tr reads of keys kc*16 + 4g + i/4 (+8), dims db*32 + 16G + 4(i%4)
   // (i = lane % 16): logical chunk 4db + x, x = 2G + (i%4)/2, stored at (4db + x) ^ vsw =
   // 4(db ^ vsw/4) + x, at byte 8(i%2) of the chunk.
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   int vcur[DB];  // offsets into the V buffer of the previous tile (V buffer 1 before tile 0)
 #pragma unroll
   for (int db = 0; db < DB; ++db)
-    vcur[db] = 3 * TILEB + vkey * ROWB + (4 * (db ^ (vsw >> 2)) + 2 * G + ((i16 & 3) >> 1)) * 16 +
+    vcur[db] = TILEB + vkey * ROWB + (4 * (db ^ (vsw >> 2)) + 2 * G + ((i16 & 3) >> 1)) * 16 +
                8 * (i16 & 1);
 
   float mref = kNegInf, lsum = 0.f;
@@ -256,7 +257,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       xsched<kKC * DB, kKB * DC, FA_FWD_PREFETCH>(
           std::make_integer_sequence<int, kKC * DB + kKB * DC>{});
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) kcur[dc] ^= TILEB;
+    for (int dc = 0; dc < DC; ++dc) kcur[dc] += kslot == 2 ? -2 * TILEB : TILEB;
+    kslot = kslot == 2 ? 0 : kslot + 1;
 #pragma unroll
     for (int db = 0; db < DB; ++db) vcur[db] ^= TILEB;
   };
@@ -336,17 +338,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int kc = 0; kc < kKC; ++kc) asm volatile("" : "+v"(pf[kc]));
   };
-  // Group B issues the direct loads at the start of its vector phase Y(t): K(t+2) into
-  // K buffer t % 2 and V(t+1) into V buffer (t+1) % 2, the buffers both groups finished reading
-  // at the previous barrier; they have landed (vmcnt 0 in the issuing waves) by the barrier
-  // that closes the next phase. (Issued in group A's matrix phases instead, they lengthen
-  // those, which are the longer phases here: 4% slower.)
+  // Each group issues one tile's direct loads at the start of its vector phase Y(t), so the
+  // load issue (the vector phases' largest extra cost) is split evenly between the phases:
+  // group A loads K(t+2) into K buffer (t+2) % 3, which last held K(t-1), read by both groups
+  // before the previous barrier; group B loads V(t+1) into V buffer (t+1) % 2, which last held
+  // V(t-1), read by both groups in their matrix phases X(t). Every wave waits for its own
+  // loads (vmcnt 0) at the end of its next matrix phase, one or two phases before the tile's
+  // first reader.
+  int kload_slot = 2;  // K buffer of tile t + 2 for the next loads(t) (uniform)
   auto loads = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 < ntiles) tload(true, (t & 1) ? Ks1 : Ks0, t + 2);
-    if (t + 1 < ntiles) tload(false, (t & 1) ? Vs0 : Vs1, t + 1);
+    if (grp == 0) {
+      if (t + 2 < ntiles) tload(true, kbuf(kload_slot), t + 2);
+      kload_slot = kload_slot == 2 ? 0 : kload_slot + 1;
+    } else if (t + 1 < ntiles) {
+      tload(false, vbuf((t + 1) & 1), t + 1);
+    }
   };
   auto finish_x = [&]() __attribute__((always_inline)) {
-    if (grp == 1) wait_vmcnt<0>();
+    wait_vmcnt<0>();
     phase_barrier();
   };
   // X(t) then Y(t), for 1 <= t < nt_w
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     xphase(I1{}, I1{});
     pin_s();
     finish_x();
-    if (grp == 1) loads(t);
+    loads(t);
     yphase(t);
     pin_p();
     phase_barrier();
@@ -362,18 +371,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 
   // Phase p: group A runs X(p/2) for even p and Y(p/2) for odd p, group B one phase later.
   // A wave's own tiles end at nt_w; it then passes the remaining barriers idle.
-  if (grp == 1) tload(true, Ks0, 0);
+  if (grp == 1) tload(true, kbuf(0), 0);
   wait_vmcnt<0>();
   phase_barrier();
   if (grp == 1) {
-    if (ntiles > 1) tload(true, Ks1, 1);
-    tload(false, Vs0, 0);
+    if (ntiles > 1) tload(true, kbuf(1), 1);
+    tload(false, vbuf(0), 0);
     phase_barrier();
   }
   xphase(I0{}, I1{});
   pin_s();
   finish_x();
-  if (grp == 1) loads(0);
+  loads(0);
   yphase(0);
   pin_p();
   phase_barrier();
@@ -384,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   xphase(I1{}, I0{});
   finish_x();
   for (; t < ntiles; ++t) {
-    if (grp == 1) loads(t);
+    loads(t);
     phase_barrier();
     finish_x();
   }
