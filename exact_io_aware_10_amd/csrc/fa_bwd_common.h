@@ -63,15 +63,16 @@ __device__ __forceinline__ void decode_work(const BwdArgs& a, int nblk, bool var
 }
 
 // ---------------------------------------------------------------- tile access helpers
-template <int D, int NW = kWaves>
+template <int D, int NW = kWaves, int ROWS = kTile>
 struct Tile {
   static constexpr int ROWB = D * 2;        // bytes per row
   static constexpr int CPR = D / 8;         // 16-byte chunks per row
-  static constexpr int BYTES = kTile * ROWB;
+  static constexpr int BYTES = ROWS * ROWB;
   static constexpr int RPL = 1024 / ROWB;   // rows per 1 KiB direct load
   static constexpr int LPW = BYTES / 1024 / NW;  // direct loads per wave per tile (NW waves)
+  static_assert(LPW >= 1 && LPW * NW * 1024 == BYTES, "whole 1 KiB loads per wave");
 
-  // direct HBM/L2 -> LDS load of tile rows [row0, row0 + kTile) of a [tokens, H, D] tensor
+  // direct HBM/L2 -> LDS load of tile rows [row0, row0 + ROWS) of a [tokens, H, D] tensor
   // (rs: the tensor's buffer resource words). Issued from inline assembly (dma16): with the
   // builtin the compiler makes the next LDS reads of the current tile wait for this
   // prefetch. The caller waits (vmcnt 0) before the barrier that precedes the tile's readers.
