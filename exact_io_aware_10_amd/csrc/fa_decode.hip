@@ -19,8 +19,9 @@
 // (the matrix cores have ample headroom at these shapes: the bound is the K/V stream).
 // Tiles use the dual chunk swizzle of the backward kernels, which keeps both the row-fragment
 // reads of K and the transposed reads of V conflict-free.
-// Kernel 2 (combine_kernel): one wave per output row merges the S partials and writes O and
-// LSE.
+// Kernel 2 (combine_kernel): one wave per output row merges the S partials (their row
+// statistics one per lane, their outputs as independent 16-byte loads over lane groups) and
+// writes O and LSE.
 #include "fa_bwd_common.h"
 #include "fa_decode.h"
 
@@ -237,41 +238,59 @@ __global__ __launch_bounds__(64 * Cfg<D>::kWaves, 1) void decode_kernel(DecodeAr
   }
 }
 
-// One wave per output row (b, q, h): merge the S partials.
+// One wave per output row (b, q, h): merge the S partials. The row statistics of up to 64
+// partials are loaded at once (one per lane) and reduced across the wave; the partial outputs
+// are then read as independent 16-byte loads, lane group j of the wave taking partials
+// s = j, j + 64/LPR, ... over D/4 lanes of four dims each, and the groups' sums are added at
+// the end. (A loop over the partials in one lane waits for one load after another.)
 template <int D, class T>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  constexpr int PER = D / 64;  // dims per lane
+  constexpr int LPR = D / 4;      // lanes per partial row (four dims each)
+  constexpr int SPW = 64 / LPR;   // partials read side by side
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= (long)a.B * a.H * a.Nq) return;
   const int qi = row % a.Nq;
   const long bh = row / a.Nq;  // b * H + h
   const int h = bh % a.H, b = bh / a.H;
-  const long part0 = bh * a.S * a.Nq + qi;
+  const long part0 = bh * a.S * a.Nq + qi;  // partial s of this row at part0 + s * Nq
+
+  // m = max_s m_s, then l = sum_s l_s 2^(m_s - m) over the ranges that saw a key
   float m = kNegInf;
-  for (int s = 0; s < a.S; ++s) m = fmaxf(m, a.mpart[part0 + (long)s * a.Nq]);
-  float acc[PER];
+  for (int s = lane; s < a.S; s += 64) m = fmaxf(m, a.mpart[part0 + (long)s * a.Nq]);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
   float l = 0.f;
-  if (m != kNegInf) {
-    for (int s = 0; s < a.S; ++s) {
+  if (m != kNegInf)
+    for (int s = lane; s < a.S; s += 64) {
       const long p = part0 + (long)s * a.Nq;
       const float ls = a.lpart[p];
-      if (ls == 0.f) continue;
-      const float wgt = exp2f_hw(a.mpart[p] - m);
-      l += ls * wgt;
-      const float* op = a.opart + p * D + lane * PER;
+      if (ls > 0.f) l += ls * exp2f_hw(a.mpart[p] - m);
+    }
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += wgt * op[e];
+  for (int x = 32; x >= 1; x >>= 1) l += __shfl_xor(l, x);
+
+  const int c4 = (lane % LPR) * 4;  // this lane's first dim
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (m != kNegInf) {
+#pragma unroll 8
+    for (int s = lane / LPR; s < a.S; s += SPW) {
+      const long p = part0 + (long)s * a.Nq;
+      const float ls = a.lpart[p];
+      const float wgt = ls > 0.f ? exp2f_hw(a.mpart[p] - m) : 0.f;
+      const f32x4 op = *reinterpret_cast<const f32x4*>(a.opart + p * D + c4);
+      acc += wgt * op;
     }
   }
+#pragma unroll
+  for (int x = LPR; x < 64; x <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], x);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  uint16_t* o = a.o + (((long)b * a.Nq + qi) * a.H + h) * D + lane * PER;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(o) = pack2<T>(acc[0] * inv, acc[1] * inv);
-  } else {
-    o[0] = (uint16_t)(pack2<T>(acc[0] * inv, 0.f) & 0xffffu);
+  if (lane < LPR) {
+    uint16_t* o = a.o + (((long)b * a.Nq + qi) * a.H + h) * D + c4;
+    *reinterpret_cast<u32x2*>(o) = u32x2{pack2<T>(acc[0] * inv, acc[1] * inv),
+                                         pack2<T>(acc[2] * inv, acc[3] * inv)};
   }
   if (lane == 0) a.lse[bh * a.Nq + qi] = l > 0.f ? (m + log2f_hw(l)) * kLn2 : kNegInf;
 }
