@@ -68,9 +68,17 @@ def fp8_inputs(B, N, H, d, seed):
     return [c for c, _ in qs], [s for _, s in qs]
 
 
-def normal_bits(shape, dtype: str, seed: int) -> np.ndarray:
+def normal_bits(shape, dtype: str, seed: int, chunk: int = 1 << 26) -> np.ndarray:
+    """N(0, 1) draws of default_rng(seed) in row-major order, rounded to dtype. Drawn and
+    rounded `chunk` values at a time from the one generator (the same stream as a single
+    draw), so a tensor of 2^30 values needs no multi-gigabyte temporaries."""
     rng = np.random.default_rng(seed)
-    return round_to_bits(rng.standard_normal(size=shape, dtype=np.float32), dtype)
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        out[a:b] = round_to_bits(rng.standard_normal(size=b - a, dtype=np.float32), dtype)
+    return out.reshape(shape)
 
 
 def attention_inputs(B, N, H, d, dtype, seed, with_dout=False):

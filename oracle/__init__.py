@@ -45,9 +45,12 @@ def _load():
         lib.oracle_bwd_varlen.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ip, L, L, L, L,
                                           D, I, I]
         lib.oracle_merge.argtypes = [dp, dp, dp, dp, L, L, L, I]
+        lp = ctypes.POINTER(ctypes.c_long)
+        lib.oracle_rows.argtypes = [dp, dp, dp, dp, lp, dp, dp, dp, L, L, L, D, I, I]
+        lib.oracle_tail_keys.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, D, I]
         for f in ("oracle_fwd", "oracle_fwd_blocked", "oracle_bwd", "oracle_fwd_varlen",
                   "oracle_bwd_varlen", "oracle_fwd_decode", "oracle_fwd_decode_split",
-                  "oracle_merge"):
+                  "oracle_merge", "oracle_rows", "oracle_tail_keys"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -202,6 +205,50 @@ def merge(o_parts, lse_parts, nthreads=None):
                               nthreads or default_threads())
     _check(rc, "oracle_merge")
     return o.reshape(B, N, H, d), np.ascontiguousarray(lse.reshape(B, N, H).transpose(0, 2, 1))
+
+
+def rows(q_rows, k, v, pos, scale, causal, dout_rows=None, nthreads=None):
+    """Rows of one (batch, head) slice too large for the whole-tensor functions. q_rows
+    [R, d] at positions pos (int [R]) of a slice with keys and values k, v [N, d]; dout_rows
+    [R, d] or None. Returns (O [R, d], LSE [R], dQ [R, d] or None) by the plain definition."""
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+    R, d = q_rows.shape
+    N = k.shape[0]
+    assert k.shape == (N, d) and v.shape == (N, d)
+    posa = np.ascontiguousarray(pos, dtype=np.int64)
+    assert posa.shape == (R,)
+    o = np.empty((R, d))
+    lse = np.empty(R)
+    dq = None
+    dptr = None
+    if dout_rows is not None:
+        dout_rows = _f64(dout_rows)
+        assert dout_rows.shape == (R, d)
+        dq = np.empty((R, d))
+        dptr = _p(dout_rows)
+    rc = _load().oracle_rows(_p(q_rows), _p(k), _p(v), dptr,
+                             posa.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), _p(o), _p(lse),
+                             _p(dq) if dq is not None else None, R, N, d, float(scale),
+                             int(causal), nthreads or default_threads())
+    _check(rc, "oracle_rows")
+    return o, lse, dq
+
+
+def tail_keys(q_tail, k, v, dout_tail, o_tail, lse_tail, scale, nthreads=None):
+    """dK, dV [R, d] of the last R keys of a causal slice (k, v [N, d]) from its last R rows
+    (q_tail, dout_tail, o_tail [R, d], lse_tail [R])."""
+    q_tail, k, v = _f64(q_tail), _f64(k), _f64(v)
+    dout_tail, o_tail, lse_tail = _f64(dout_tail), _f64(o_tail), _f64(lse_tail)
+    R, d = q_tail.shape
+    N = k.shape[0]
+    assert k.shape == (N, d) and v.shape == (N, d) and lse_tail.shape == (R,)
+    dk = np.empty((R, d))
+    dv = np.empty((R, d))
+    rc = _load().oracle_tail_keys(_p(q_tail), _p(k), _p(v), _p(dout_tail), _p(o_tail),
+                                  _p(lse_tail), _p(dk), _p(dv), R, N, d, float(scale),
+                                  nthreads or default_threads())
+    _check(rc, "oracle_tail_keys")
+    return dk, dv
 
 
 def _cu(cu_seqlens):

@@ -489,4 +489,86 @@ int oracle_merge(const double* o_parts, const double* lse_parts, double* o, doub
   return 0;
 }
 
+// Spot checks of problems too large for the whole-tensor functions, one (batch, head) slice
+// at a time: q_rows, dout_rows [R, d] are R query rows at positions pos[r] of a slice whose
+// keys and values k, v are [N, d]. For each row, by the plain definition: O, LSE and, when
+// dout_rows is given, dQ = scale * sum_j P_ij (dP_ij - D_i) k_j with D_i = <dO_i, O_i>.
+int oracle_rows(const double* q_rows, const double* k, const double* v, const double* dout_rows,
+                const long* pos, double* o, double* lse, double* dq, long R, long N, long d,
+                double scale, int causal, int nthreads) {
+  if (R < 0 || N < 0 || d <= 0) return -1;
+  for (long r = 0; r < R; ++r)
+    if (pos[r] < 0 || pos[r] >= N) return -2;
+  parallel_for(R, nthreads, [&](long r) {
+    const long je = visible_end(pos[r], N, causal);
+    const double* qr = q_rows + r * d;
+    double* orow = o + r * d;
+    for (long c = 0; c < d; ++c) orow[c] = 0.0;
+    if (dout_rows != nullptr)
+      for (long c = 0; c < d; ++c) dq[r * d + c] = 0.0;
+    if (je == 0) {
+      lse[r] = kNegInf;
+      return;
+    }
+    std::vector<double> sc(je);
+    double m = kNegInf;
+    for (long j = 0; j < je; ++j) {
+      sc[j] = scale * dot(qr, k + j * d, d);
+      m = std::max(m, sc[j]);
+    }
+    double l = 0.0;
+    for (long j = 0; j < je; ++j) {
+      const double p = std::exp(sc[j] - m);
+      l += p;
+      for (long c = 0; c < d; ++c) orow[c] += p * v[j * d + c];
+    }
+    for (long c = 0; c < d; ++c) orow[c] /= l;
+    lse[r] = m + std::log(l);
+    if (dout_rows == nullptr) return;
+    const double* dor = dout_rows + r * d;
+    const double Di = dot(dor, orow, d);
+    double* dqr = dq + r * d;
+    for (long j = 0; j < je; ++j) {
+      const double P = std::exp(sc[j] - lse[r]);
+      const double dS = P * (dot(dor, v + j * d, d) - Di);
+      for (long c = 0; c < d; ++c) dqr[c] += dS * k[j * d + c];
+    }
+    for (long c = 0; c < d; ++c) dqr[c] *= scale;
+  });
+  return 0;
+}
+
+// Under the causal mask, key j is seen only by query rows i >= j, so the gradients of the
+// last R keys of a slice need only its last R rows. Given those rows (q_tail, dout_tail
+// [R, d], rows N - R .. N - 1) with their O and LSE (o_tail [R, d], lse_tail [R], e.g. from
+// oracle_rows) and the slice's k, v [N, d]: dV_j = sum_{i >= j} P_ij dO_i and
+// dK_j = scale * sum_{i >= j} dS_ij q_i for j = N - R .. N - 1, into dk, dv [R, d].
+int oracle_tail_keys(const double* q_tail, const double* k, const double* v,
+                     const double* dout_tail, const double* o_tail, const double* lse_tail,
+                     double* dk, double* dv, long R, long N, long d, double scale, int nthreads) {
+  if (R < 0 || R > N || d <= 0) return -1;
+  const long t0 = N - R;
+  parallel_for(R, nthreads, [&](long c) {
+    const long j = t0 + c;
+    const double* kj = k + j * d;
+    const double* vj = v + j * d;
+    double* dkj = dk + c * d;
+    double* dvj = dv + c * d;
+    for (long e = 0; e < d; ++e) dkj[e] = dvj[e] = 0.0;
+    for (long r = c; r < R; ++r) {  // rows i = t0 + r >= j
+      const double* qi = q_tail + r * d;
+      const double* doi = dout_tail + r * d;
+      const double Di = dot(doi, o_tail + r * d, d);
+      const double P = std::exp(scale * dot(qi, kj, d) - lse_tail[r]);
+      const double dS = P * (dot(doi, vj, d) - Di);
+      for (long e = 0; e < d; ++e) {
+        dvj[e] += P * doi[e];
+        dkj[e] += dS * qi[e];
+      }
+    }
+    for (long e = 0; e < d; ++e) dkj[e] *= scale;
+  });
+  return 0;
+}
+
 }  // extern "C"

@@ -42,6 +42,9 @@ MUTANTS = {
     "merge_drops_l": ("const double w = ls[t] * std::exp(ms[t] - m);",
                       "const double w = std::exp(ms[t] - m);"),
     "merge_lse_drops_max": ("lse = m + std::log(l);", "lse = std::log(l);"),
+    "rows_dq_scale_dropped": ("for (long c = 0; c < d; ++c) dqr[c] *= scale;", ""),
+    "tail_keys_skip_diagonal": ("for (long r = c; r < R; ++r) {",
+                                "for (long r = c + 1; r < R; ++r) {"),
 }
 
 

@@ -609,3 +609,46 @@ def test_merge_empty_parts():
     b = oracle.merge(np.stack([o2, o1]), np.stack([l2, l1]))
     np.testing.assert_allclose(a[0], b[0], atol=1e-14)
     np.testing.assert_allclose(a[1], b[1], atol=1e-14)
+
+
+# ---------------------------------------------------------------- row-subset functions
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_equal_whole_tensor_oracle(causal):
+    """oracle.rows (O, LSE, dQ of chosen rows against all keys) gives the rows of the
+    whole-tensor fwd and bwd, which the pins above fix."""
+    N, H, d = 57, 2, 16
+    q, k, v, do = (_rand((1, N, H, d), 60 + i) for i in range(4))
+    o, lse = oracle.fwd(q, k, v, 0.3, causal)
+    dq, _, _ = oracle.bwd(q, k, v, o, lse, do, 0.3, causal)
+    pos = np.array([0, 1, 5, 31, N - 2, N - 1])
+    for h in range(H):
+        ro, rl, rdq = oracle.rows(q[0, pos, h], k[0, :, h], v[0, :, h], pos, 0.3, causal,
+                                  do[0, pos, h])
+        np.testing.assert_allclose(ro, o[0, pos, h], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(rl, lse[0, h, pos], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(rdq, dq[0, pos, h], rtol=0, atol=1e-13)
+
+
+def test_tail_keys_equal_whole_tensor_oracle():
+    """Under the causal mask the last R keys are seen only by the last R rows: their dK and
+    dV from those rows alone equal the whole-tensor bwd's."""
+    N, H, d, R = 64, 2, 8, 9
+    q, k, v, do = (_rand((1, N, H, d), 70 + i) for i in range(4))
+    o, lse = oracle.fwd(q, k, v, 0.5, True)
+    _, dk, dv = oracle.bwd(q, k, v, o, lse, do, 0.5, True)
+    tail = np.arange(N - R, N)
+    for h in range(H):
+        to, tl, _ = oracle.rows(q[0, tail, h], k[0, :, h], v[0, :, h], tail, 0.5, True)
+        tdk, tdv = oracle.tail_keys(q[0, tail, h], k[0, :, h], v[0, :, h], do[0, tail, h],
+                                    to, tl, 0.5)
+        np.testing.assert_allclose(tdk, dk[0, tail, h], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(tdv, dv[0, tail, h], rtol=0, atol=1e-13)
+
+
+def test_chunked_draws_are_one_stream():
+    """inputs.normal_bits draws in chunks from one generator: the same bits as one draw."""
+    ref = inputs.round_to_bits(
+        np.random.default_rng(7).standard_normal(size=(3, 1001, 5), dtype=np.float32), "bf16")
+    for chunk in (1, 7, 1000, 1 << 26):
+        assert np.array_equal(inputs.normal_bits((3, 1001, 5), "bf16", 7, chunk=chunk), ref)
