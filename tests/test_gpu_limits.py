@@ -86,3 +86,42 @@ def test_splitkv_at_size_limit():
     ro, rl = oracle.fwd_decode(w(qb), w(kb), w(vb), scale, True)
     assert_close("O", f64_of(o, "bf16"), ro)
     assert_close("LSE", lse.cpu().numpy().astype(np.float64), rl)
+
+
+@pytest.mark.timeout(900)
+def test_varlen_beyond_2gib():
+    """Packed sequences past the first 2 GiB of each tensor: T = 1 100 000 tokens (lengths
+    drawn as in the packed workload, seed 40), H16 d128 bf16 causal, forward and backward.
+    The sequence limit applies per sequence; the sequences' base offsets are 64-bit. The
+    oracle recomputes the first sequence that starts beyond 2^31 bytes (head 0) and the last
+    one (head 15) as dense problems."""
+    import torch
+    T = 1_100_000
+    lens = inputs.varlen_lengths(T, 64, 16384, 40)
+    cu = inputs.cu_seqlens(lens)
+    print(f"[limit varlen] T={T} nseq={len(lens)} H={H} d={D} bf16 causal", flush=True)
+    bits = [inputs.normal_bits((T, H, D), "bf16", 41 + i) for i in range(4)]
+    q, k, v, do = (to_device(x, "bf16") for x in bits)
+    cu_d = torch.from_numpy(cu).cuda()
+    o, lse = fa().fa_fwd_varlen(q, k, v, cu_d, max(lens), causal=True)
+    dq, dk, dv = fa().fa_bwd_varlen(q, k, v, o, lse, do, cu_d, max(lens), causal=True)
+    torch.cuda.synchronize()
+    print("  kernels done", flush=True)
+    start_bytes = cu[:-1].astype(np.int64) * H * D * 2
+    beyond = int(np.argmax(start_bytes >= 1 << 31))
+    assert start_bytes[beyond] >= 1 << 31
+    scale = 1 / math.sqrt(D)
+    w = lambda x: oracle.widen(x, "bf16")
+    for s, h in ((beyond, 0), (len(lens) - 1, H - 1)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        print(f"  sequence {s}: tokens {a}..{b} (byte offset {a * H * D * 2}), head {h}",
+              flush=True)
+        sl = lambda x: w(x[a:b, h:h + 1][None])
+        qs, ks, vs, dos = (sl(x) for x in bits)
+        ro, rl = oracle.fwd(qs, ks, vs, scale, True)
+        rq, rk, rv = oracle.bwd(qs, ks, vs, ro, rl, dos, scale, True)
+        g = lambda t: f64_of(t[a:b, h:h + 1], "bf16")[None]
+        assert_close("O", g(o), ro)
+        assert_close("LSE", lse[h, a:b].cpu().numpy().astype(np.float64)[None, None], rl)
+        for name, t, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            assert_close(name, g(t), r)
