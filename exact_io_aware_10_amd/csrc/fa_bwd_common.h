@@ -53,13 +53,26 @@ __device__ __forceinline__ SliceInfo slice_info(const BwdArgs& a, int bs, int h)
 }
 
 // Work item of a dense or packed launch: (block index within the slice, head, batch/seq).
-__device__ __forceinline__ void decode_work(const BwdArgs& a, int nblk, bool varlen, int& blk,
-                                            int& h, int& bs) {
+// With causal set, dense launches go longest first over whole slices per XCD (causal_order)
+// and the costliest block is taken to be the last one (long_last: query blocks); packed
+// launches then reverse the block order within each sequence.
+__device__ __forceinline__ void decode_work(const BwdArgs& a, int nblk, bool varlen,
+                                            bool causal, bool long_last, int& blk, int& h,
+                                            int& bs) {
+  if (causal && !varlen) {
+    int rank, bh;
+    causal_order(blockIdx.x, a.B * a.H, rank, bh);
+    blk = long_last ? nblk - 1 - rank : rank;
+    h = bh % a.H;
+    bs = bh / a.H;
+    return;
+  }
   uint32_t w = blockIdx.x;
   if (!varlen) w = xcd_remap(w, gridDim.x);
   blk = w % nblk;
   h = (w / nblk) % a.H;
   bs = w / (nblk * a.H);
+  if (causal && long_last) blk = nblk - 1 - blk;  // longest rows first within a sequence
 }
 
 // ---------------------------------------------------------------- tile access helpers

@@ -32,8 +32,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   Lanes<D> ln(lane);
   const int nqb = (a.N + BQ - 1) / BQ;
   int qb, h, bs;
-  decode_work(a, nqb, VARLEN, qb, h, bs);
-  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+  decode_work(a, nqb, VARLEN, CAUSAL, true, qb, h, bs);
   const SliceInfo si = slice_info(a, bs, h);
   const int L = si.L;
   const int q0 = qb * BQ;

@@ -229,4 +229,23 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t lin, uint32_t total) {
   return x * q + (x < r ? x : r) + slot;
 }
 
+// Work order for causal launches over items (bh, r) whose cost falls with the rank r (r = 0
+// is the longest). The hardware deals workgroups round-robin over the 8 XCDs and each XCD
+// starts its share in order; here XCD x keeps a contiguous range of whole (b, h) slices (their
+// K/V share its L2) and hands out all of their rank-0 items, then all rank-1 items, and so
+// on: longest first across the slices, so no long item is left for the end. When the slices
+// do not split evenly over the XCDs the order is rank-major over all slices.
+__device__ __forceinline__ void causal_order(uint32_t lin, int nbh, int& rank, int& bh) {
+  const uint32_t nx = 8;
+  if (nbh % nx == 0) {
+    const uint32_t per = nbh / nx;  // slices per XCD
+    const uint32_t x = lin % nx, slot = lin / nx;
+    rank = (int)(slot / per);
+    bh = (int)(x * per + slot % per);
+  } else {
+    rank = (int)(lin / (uint32_t)nbh);
+    bh = (int)(lin % (uint32_t)nbh);
+  }
+}
+
 }  // namespace fa

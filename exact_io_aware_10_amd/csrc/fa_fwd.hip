@@ -121,12 +121,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 
   // ---- work item: (query block, head, batch or sequence)
   const int nqb = (a.N + BQ - 1) / BQ;
-  uint32_t w = blockIdx.x;
-  if (!VARLEN) w = xcd_remap(w, gridDim.x);
-  int qb = w % nqb;
-  const int h = (w / nqb) % a.H;
-  const int bs = w / (nqb * a.H);
-  if (CAUSAL || VARLEN) qb = nqb - 1 - qb;  // longest rows first
+  int qb, h, bs;
+  if (CAUSAL && !VARLEN) {  // longest rows first over whole slices per XCD
+    int rank, bh;
+    causal_order(blockIdx.x, a.B * a.H, rank, bh);
+    qb = nqb - 1 - rank;
+    h = bh % a.H;
+    bs = bh / a.H;
+  } else {
+    uint32_t w = blockIdx.x;
+    if (!VARLEN) w = xcd_remap(w, gridDim.x);
+    qb = w % nqb;
+    h = (w / nqb) % a.H;
+    bs = w / (nqb * a.H);
+    if (VARLEN) qb = nqb - 1 - qb;  // longest rows first
+  }
 
   long tok0;
   int L;

@@ -155,11 +155,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   // ---- work item: (query block, head, batch)
   const int nqb = (a.N + BQ - 1) / BQ;
-  const uint32_t w = xcd_remap(blockIdx.x, gridDim.x);
-  int qb = w % nqb;
-  const int h = (w / nqb) % a.H;
-  const int bs = w / (nqb * a.H);
-  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+  int qb, h, bs;
+  if (CAUSAL) {  // longest rows first over whole slices per XCD
+    int rank, bh;
+    causal_order(blockIdx.x, a.B * a.H, rank, bh);
+    qb = nqb - 1 - rank;
+    h = bh % a.H;
+    bs = bh / a.H;
+  } else {
+    const uint32_t w = xcd_remap(blockIdx.x, gridDim.x);
+    qb = w % nqb;
+    h = (w / nqb) % a.H;
+    bs = w / (nqb * a.H);
+  }
   const int L = a.N;
   const long tok0 = (long)bs * a.N;
   const int q0 = qb * BQ;
