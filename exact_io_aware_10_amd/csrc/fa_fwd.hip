@@ -33,6 +33,7 @@
 //    running max used as the exponent's reference is only moved when the true row max
 //    exceeds it by more than 8 (in log2 units), so the rescale of the output accumulator is
 //    rare; O = acc / l and LSE = (m_ref + log2 l) ln 2 are exact for any reference.
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -92,8 +93,14 @@ __device__ __forceinline__ void xsched(std::integer_sequence<int, M...>) {
   (xsched_step<NPV, NM, PD, M>(), ...);
 }
 
-template <int D, class T, bool CAUSAL, bool VARLEN>
+// STREAM (dense, no mask): one workgroup per CU takes items blockIdx.x, blockIdx.x + G, ...
+// (G = gridDim.x) of the XCD-remapped work list, as one continuous stream of key/value tiles:
+// the next item's first tiles are loaded through the same buffers and its Q rows into spare
+// registers while the current item finishes, and an item's output is stored during the
+// vector phase that starts the next item, so the pipeline never drains between items.
+template <int D, class T, bool CAUSAL, bool VARLEN, bool STREAM>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
+  static_assert(!STREAM || (!CAUSAL && !VARLEN), "the stream form is for dense, unmasked launches");
   constexpr int BQ = 32 * kWaves;
   constexpr int ROWB = D * 2;                 // bytes per K/V row in LDS
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -121,8 +128,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 
   // ---- work item: (query block, head, batch or sequence)
   const int nqb = (a.N + BQ - 1) / BQ;
+  const uint32_t total = (uint32_t)nqb * a.H * a.B;  // items of the launch
+  // item j of this workgroup in the stream form
+  auto stream_item = [&](int j, int& iqb, int& ih, int& ibs) __attribute__((always_inline)) {
+    const uint32_t w = xcd_remap(blockIdx.x + (uint32_t)j * gridDim.x, total);
+    iqb = w % nqb;
+    ih = (w / nqb) % a.H;
+    ibs = w / (nqb * a.H);
+  };
+  const int nitems = STREAM ? (int)((total - blockIdx.x + gridDim.x - 1) / gridDim.x) : 1;
   int qb, h, bs;
-  if (CAUSAL && !VARLEN) {  // longest rows first over whole slices per XCD
+  if (STREAM) {
+    stream_item(0, qb, h, bs);
+  } else if (CAUSAL && !VARLEN) {  // longest rows first over whole slices per XCD
     int rank, bh;
     causal_order(blockIdx.x, a.B * a.H, rank, bh);
     qb = nqb - 1 - rank;
@@ -149,26 +167,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     L = a.N;
     tok0 = (long)bs * a.N;
   }
-  const int q0 = qb * BQ;
+  int q0 = qb * BQ;
   if (q0 >= L) return;
 
   const uint32_t rstride = (uint32_t)a.H * D * 2;  // bytes between consecutive tokens
-  const long base = (tok0 * a.H + h) * D;
+  long base = (tok0 * a.H + h) * D;
   const uint32_t nbytes = (uint32_t)(L - 1) * rstride + D * 2;
-  const auto rq = make_rsrc(a.q + base, nbytes);
-  const auto ro = make_rsrc(a.o + base, nbytes);
+  auto ro = make_rsrc(a.o + base, nbytes);
   float* lse = a.lse + (VARLEN ? (long)h * a.T + tok0 : ((long)bs * a.H + h) * a.N);
 
-  const int wq0 = q0 + rb * 32;  // first query row of this wave
-  const int qi = wq0 + l32;        // this lane's query row
+  int wq0 = q0 + rb * 32;  // first query row of this wave
+  int qi = wq0 + l32;        // this lane's query row
   const int kend = CAUSAL ? (L < q0 + BQ ? L : q0 + BQ) : L;
   const int ntiles = (kend + kBK - 1) / kBK;
+  const int ntiles_c = ntiles;             // tiles per item (the same for every item)
+  const int nstream = nitems * ntiles;     // tiles of the whole stream
 
   // ---- Q rows into registers (B operand of S^T = K Q^T): d = 16*dc + 8g .. +7
-  u32x4 qreg[DC];
+  auto load_q = [&](u32x4 (&dst)[DC], long qbase, int row) __attribute__((always_inline)) {
+    const auto rq = make_rsrc(a.q + qbase, nbytes);
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc)
-    qreg[dc] = buf_load16(rq, (uint32_t)qi * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
+    for (int dc = 0; dc < DC; ++dc)
+      dst[dc] = buf_load16(rq, (uint32_t)row * rstride + (16 * dc + 8 * g) * 2) ^ a.qsign;
+  };
+  u32x4 qreg[DC];
+  load_q(qreg, base, qi);
 
   // ---- direct HBM/L2 -> LDS tile loads: this wave fills LPW 1 KiB blocks of each tile;
   // lane l of a block writes row blk*RPL + l/CPR, physical chunk l%CPR. Issued from inline
@@ -187,16 +210,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     kof[j] = (uint32_t)lrow * rstride + (uint32_t)((lpc ^ kswz<D>(row)) * 16);
     vof[j] = (uint32_t)lrow * rstride + (uint32_t)((lpc ^ vswz<D>(row)) * 16);
   }
-  auto tload_one = [&](bool is_k, uint8_t* tile, int t, int j) __attribute__((always_inline)) {
+  auto tload_one = [&](u32x4 words, bool is_k, uint8_t* tile, int t, int j)
+      __attribute__((always_inline)) {
     const int blk = (wave & 3) * LPW + j;
     const uint32_t m0 =
         __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(tile - smem) + blk * 1024);
-    dma16s<0>(is_k ? wk : wv, m0, is_k ? kof[j] : vof[j],
-              (uint32_t)(t * kBK + blk * RPL) * rstride);
+    dma16s<0>(words, m0, is_k ? kof[j] : vof[j], (uint32_t)(t * kBK + blk * RPL) * rstride);
   };
-  auto tload = [&](bool is_k, uint8_t* tile, int t) __attribute__((always_inline)) {
+  // buffer resource words of K or V for item j of the stream form
+  auto item_words = [&](int j, bool is_k) __attribute__((always_inline)) {
+    int jqb, jh, jbs;
+    stream_item(j, jqb, jh, jbs);
+    return rsrc_words((is_k ? a.k : a.v) + ((long)jbs * a.N * a.H + jh) * D, nbytes);
+  };
+  auto tload_w = [&](u32x4 words, bool is_k, uint8_t* tile, int t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) tload_one(is_k, tile, t, j);
+    for (int j = 0; j < LPW; ++j) tload_one(words, is_k, tile, t, j);
+  };
+  // tile s of the stream (prologue): tile s of this item, or (stream form) tile s % ntiles
+  // of item s / ntiles
+  auto tload = [&](bool is_k, uint8_t* tile, int s) __attribute__((always_inline)) {
+    if (STREAM) {
+      const int j = s / ntiles_c;
+      tload_w(item_words(j, is_k), is_k, tile, s - j * ntiles_c);
+    } else {
+      tload_w(is_k ? wk : wv, is_k, tile, s);
+    }
   };
 
   // ---- per-lane LDS byte offsets of the MFMA operand reads, relative to a tile buffer.
@@ -355,18 +394,40 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // loads (vmcnt 0) at the end of its next matrix phase, one or two phases before the tile's
   // first reader.
   int kload_slot = 2;  // K buffer of tile t + 2 for the next loads(t) (uniform)
+  // Position of the next tile each group loads (item, tile within the item) and that item's
+  // resource words, advanced one tile per call: K from stream tile 2 on, V from tile 1 on.
+  int kl_j = STREAM ? 2 / ntiles_c : 0, kl_t = STREAM ? 2 - kl_j * ntiles_c : 2;
+  int vl_j = STREAM ? 1 / ntiles_c : 0, vl_t = STREAM ? 1 - vl_j * ntiles_c : 1;
+  u32x4 kl_w = wk, vl_w = wv;
+  if (STREAM) {
+    if (grp == 0 && kl_j > 0 && kl_j < nitems) kl_w = item_words(kl_j, true);
+    if (grp == 1 && vl_j > 0 && vl_j < nitems) vl_w = item_words(vl_j, false);
+  }
   auto loads = [&](int t) __attribute__((always_inline)) {
     if (grp == 0) {
-      if (t + 2 < ntiles) tload(true, kbuf(kload_slot), t + 2);
+      if (t + 2 < nstream) {
+        tload_w(kl_w, true, kbuf(kload_slot), kl_t);
+        if (STREAM && ++kl_t == ntiles_c) {
+          kl_t = 0;
+          if (++kl_j < nitems) kl_w = item_words(kl_j, true);
+        }
+        if (!STREAM) ++kl_t;
+      }
       kload_slot = kload_slot == 2 ? 0 : kload_slot + 1;
-    } else if (t + 1 < ntiles) {
-      tload(false, vbuf((t + 1) & 1), t + 1);
+    } else if (t + 1 < nstream) {
+      tload_w(vl_w, false, vbuf((t + 1) & 1), vl_t);
+      if (STREAM && ++vl_t == ntiles_c) {
+        vl_t = 0;
+        if (++vl_j < nitems) vl_w = item_words(vl_j, false);
+      }
+      if (!STREAM) ++vl_t;
     }
   };
   auto finish_x = [&]() __attribute__((always_inline)) {
     wait_vmcnt<0>();
     phase_barrier();
   };
+
   // X(t) then Y(t), for 1 <= t < nt_w
   auto step = [&](int t) __attribute__((always_inline)) {
     xphase(I1{}, I1{});
@@ -378,49 +439,117 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     phase_barrier();
   };
 
+  // ---- epilogue of an item: O = acc / l (rows >= L are dropped by the buffer bounds), LSE
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    const float l = pair_sum(lsum);
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x16& o = oacc[db];
+        u32x2 v = {pack2<T>(o[4 * rr] * inv, o[4 * rr + 1] * inv),
+                   pack2<T>(o[4 * rr + 2] * inv, o[4 * rr + 3] * inv)};
+        buf_store8(ro, (uint32_t)qi * rstride + (db * 32 + 8 * rr + 4 * g) * 2, v);
+      }
+    if (g == 0 && qi < L) lse[qi] = l > 0.f ? (mref + log2f_hw(l)) * kLn2 : kNegInf;
+  };
+
   // Phase p: group A runs X(p/2) for even p and Y(p/2) for odd p, group B one phase later.
   // A wave's own tiles end at nt_w; it then passes the remaining barriers idle.
   if (grp == 1) tload(true, kbuf(0), 0);
   wait_vmcnt<0>();
   phase_barrier();
   if (grp == 1) {
-    if (ntiles > 1) tload(true, kbuf(1), 1);
+    if (nstream > 1) tload(true, kbuf(1), 1);
     tload(false, vbuf(0), 0);
     phase_barrier();
   }
+  // stream form: once the matrix phase has computed S of an item's last tile, Q is free and
+  // the next item's rows are loaded into it (the next matrix phase waits for them)
+  auto next_q = [&](int j) __attribute__((always_inline)) {
+    if (STREAM && j < nitems) {
+      int jqb, jh, jbs;
+      stream_item(j, jqb, jh, jbs);
+      load_q(qreg, ((long)jbs * a.N * a.H + jh) * D, jqb * BQ + rb * 32 + l32);
+    }
+  };
   xphase(I0{}, I1{});
   pin_s();
   finish_x();
   loads(0);
+  if (ntiles == 1) next_q(1);
   yphase(0);
   pin_p();
   phase_barrier();
-  int t = 1;
+  if constexpr (STREAM) {
+    // stream step gs computes S of tile tin of item j (after the boundary, tile 0 of the
+    // next item) and P V of the stream's previous tile
+    int j = 0, tin = 1;
 #pragma unroll 1
-  for (; t < nt_w; ++t) step(t);
-  // t == nt_w: the last P V
-  xphase(I1{}, I0{});
-  finish_x();
-  for (; t < ntiles; ++t) {
-    loads(t);
-    phase_barrier();
-    finish_x();
-  }
-  if (grp == 0) phase_barrier();
-
-  // ---- epilogue: O = acc / l (rows >= L are dropped by the buffer bounds), LSE
-  const float l = pair_sum(lsum);
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
+    for (int gs = 1; gs < nstream; ++gs) {
+      const bool boundary = tin == ntiles;
+      xphase(I1{}, I1{});
+      pin_s();
+      finish_x();
+      loads(gs);
+      if (boundary) {
+        // item j is complete (its last P V ran in this matrix phase): store it, move on
+        epilogue();
+        ++j;
+        stream_item(j, qb, h, bs);
+        q0 = qb * BQ;
+        base = ((long)bs * a.N * a.H + h) * D;
+        ro = make_rsrc(a.o + base, nbytes);
+        lse = a.lse + ((long)bs * a.H + h) * a.N;
+        wq0 = q0 + rb * 32;
+        qi = wq0 + l32;
+        mref = kNegInf;
+        lsum = 0.f;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const f32x16& o = oacc[db];
-      u32x2 v = {pack2<T>(o[4 * rr] * inv, o[4 * rr + 1] * inv),
-                 pack2<T>(o[4 * rr + 2] * inv, o[4 * rr + 3] * inv)};
-      buf_store8(ro, (uint32_t)qi * rstride + (db * 32 + 8 * rr + 4 * g) * 2, v);
+        for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+        tin = 0;
+      }
+      if (tin == ntiles - 1) next_q(j + 1);
+      yphase(tin);
+      pin_p();
+      phase_barrier();
+      ++tin;
     }
-  if (g == 0 && qi < L) lse[qi] = l > 0.f ? (mref + log2f_hw(l)) * kLn2 : kNegInf;
+    // the last P V of the last item
+    xphase(I1{}, I0{});
+    finish_x();
+    if (grp == 0) phase_barrier();
+    epilogue();
+  } else {
+    int t = 1;
+#pragma unroll 1
+    for (; t < nt_w; ++t) step(t);
+    // t == nt_w: the last P V
+    xphase(I1{}, I0{});
+    finish_x();
+    for (; t < ntiles; ++t) {
+      loads(t);
+      phase_barrier();
+      finish_x();
+    }
+    if (grp == 0) phase_barrier();
+    epilogue();
+  }
+}
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 template <int D, class T, bool CAUSAL, bool VARLEN>
@@ -429,7 +558,17 @@ hipError_t launch(const FwdArgs& a, hipStream_t st) {
   const int nqb = (a.N + BQ - 1) / BQ;
   const long total = (long)nqb * a.H * a.B;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)total),
+  if constexpr (!CAUSAL && !VARLEN) {
+    // one workgroup per CU (a multiple of the 8 XCDs), each taking a stream of items, when
+    // there are at least two items per workgroup
+    const int ncu = cu_count() / 8 * 8;
+    if (ncu > 0 && total >= 2L * ncu) {
+      hipLaunchKernelGGL((fwd_kernel<D, T, false, false, true>), dim3((unsigned)ncu),
+                         dim3(kThreads), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, VARLEN, false>), dim3((unsigned)total),
                      dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }

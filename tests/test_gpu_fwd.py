@@ -90,6 +90,23 @@ def test_fwd_workload(name):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
 
 
+# Dense launches without the mask and with at least two query blocks per CU (512 on MI355X)
+# take the stream form: one workgroup per CU walking its blocks as one stream of key/value
+# tiles. Items of one tile, of two tiles with a ragged last one, of 17 blocks x 33 tiles,
+# d = 64 and fp16: all slices of the small shapes, sampled slices of the large one.
+@pytest.mark.parametrize("B,N,H,d,dtype", [(32, 100, 16, 128, "bf16"), (32, 200, 16, 64, "f16"),
+                                           (2, 4196, 16, 128, "bf16"), (4, 2048, 16, 64, "bf16")])
+def test_fwd_stream(B, N, H, d, dtype):
+    (qb, kb, vb), o, lse = run_dense(B, N, H, d, dtype, False, seed=N + H)
+    if N <= 256:
+        w = lambda x: oracle.widen(x, dtype)
+        ro, rlse = oracle.fwd(w(qb), w(kb), w(vb), 1 / math.sqrt(d), False)
+        assert_close("O", o, ro)
+        assert_close("LSE", lse, rlse)
+    else:
+        _check_slices(qb, kb, vb, o, lse, dtype, False, [(0, 0), (B - 1, H - 1), (B // 2, 7)])
+
+
 def run_varlen(lens, H, d, dtype, causal, seed, max_seqlen=None):
     import torch
     cu = inputs.cu_seqlens(lens)
