@@ -33,7 +33,6 @@
 //    running max used as the exponent's reference is only moved when the true row max
 //    exceeds it by more than 8 (in log2 units), so the rescale of the output accumulator is
 //    rare; O = acc / l and LSE = (m_ref + log2 l) ln 2 are exact for any reference.
-#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -536,20 +535,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     if (grp == 0) phase_barrier();
     epilogue();
   }
-}
-
-// Compute units of the current device (queried once per device).
-int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
 }
 
 template <int D, class T, bool CAUSAL, bool VARLEN>

@@ -128,8 +128,13 @@ __device__ __forceinline__ void xsched(std::integer_sequence<int, M...>) {
   (xsched_step<DB, NM, PD, M>(), ...);
 }
 
-template <int D, bool CAUSAL>
+// STREAM (no mask): one workgroup per CU takes items blockIdx.x, blockIdx.x + G, ... of the
+// XCD-remapped work list as one stream of key/value tiles (as the 16-bit forward's stream
+// form): the loads run on into the next item's tiles, the next item's Q rows are loaded after
+// their last use, and an item's output is stored in the vector phase that starts the next.
+template <int D, bool CAUSAL, bool STREAM>
 __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
+  static_assert(!STREAM || !CAUSAL, "the stream form is for unmasked launches");
   constexpr int BQ = 32 * kWaves;
   constexpr int ROWB = D;                     // bytes per K/V row in LDS
   constexpr int CPR = D / 16;                 // 16-byte chunks per row
@@ -155,8 +160,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   // ---- work item: (query block, head, batch)
   const int nqb = (a.N + BQ - 1) / BQ;
+  const uint32_t total = (uint32_t)nqb * a.H * a.B;
+  auto stream_item = [&](int j, int& iqb, int& ih, int& ibs) __attribute__((always_inline)) {
+    const uint32_t w = xcd_remap(blockIdx.x + (uint32_t)j * gridDim.x, total);
+    iqb = w % nqb;
+    ih = (w / nqb) % a.H;
+    ibs = w / (nqb * a.H);
+  };
+  const int nitems = STREAM ? (int)((total - blockIdx.x + gridDim.x - 1) / gridDim.x) : 1;
   int qb, h, bs;
-  if (CAUSAL) {  // longest rows first over whole slices per XCD
+  if (STREAM) {
+    stream_item(0, qb, h, bs);
+  } else if (CAUSAL) {  // longest rows first over whole slices per XCD
     int rank, bh;
     causal_order(blockIdx.x, a.B * a.H, rank, bh);
     qb = nqb - 1 - rank;
@@ -170,30 +185,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   }
   const int L = a.N;
   const long tok0 = (long)bs * a.N;
-  const int q0 = qb * BQ;
+  int q0 = qb * BQ;
   if (q0 >= L) return;
 
   const uint32_t rstride = (uint32_t)a.H * D;  // bytes between consecutive tokens (fp8)
-  const long base = (tok0 * a.H + h) * D;
+  long base = (tok0 * a.H + h) * D;
   const uint32_t nbytes = (uint32_t)(L - 1) * rstride + D;
-  const auto rq = make_rsrc(a.q + base, nbytes);
-  const auto ro = make_rsrc(a.o + base, 2 * nbytes);  // bf16 output: twice the byte offsets
+  auto ro = make_rsrc(a.o + base, 2 * nbytes);  // bf16 output: twice the byte offsets
   float* lse = a.lse + ((long)bs * a.H + h) * a.N;
 
-  const int wq0 = q0 + rb * 32;
-  const int qi = wq0 + l32;
+  int wq0 = q0 + rb * 32;
+  int qi = wq0 + l32;
   const int kend = CAUSAL ? (L < q0 + BQ ? L : q0 + BQ) : L;
   const int ntiles = (kend + kBK - 1) / kBK;
+  const int nstream = nitems * ntiles;  // tiles of the whole stream
 
   // ---- Q rows into registers (B operand of S^T = K Q^T): d = 64 dc + 32 g + byte
   u32x8 qreg[DC];
+  auto load_q = [&](long qbase, int row) __attribute__((always_inline)) {
+    const auto rq = make_rsrc(a.q + qbase, nbytes);
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    const uint32_t off = (uint32_t)qi * rstride + 64 * dc + 32 * g;
-    const u32x4 lo = buf_load16(rq, off) ^ a.qsign;
-    const u32x4 hi = buf_load16(rq, off + 16) ^ a.qsign;
-    qreg[dc] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
+    for (int dc = 0; dc < DC; ++dc) {
+      const uint32_t off = (uint32_t)row * rstride + 64 * dc + 32 * g;
+      const u32x4 lo = buf_load16(rq, off) ^ a.qsign;
+      const u32x4 hi = buf_load16(rq, off + 16) ^ a.qsign;
+      qreg[dc] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  load_q(base, qi);
 
   // ---- direct HBM/L2 -> LDS tile loads: this wave fills LPW 1 KiB blocks of a tile; lane l
   // of a block writes row blk*RPL + l/CPR, physical chunk l%CPR.
@@ -202,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   // make the matrix phase's LDS reads wait for these loads to land.
   const u32x4 wk = rsrc_words(a.k + base, nbytes), wv = rsrc_words(a.v + base, nbytes);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  auto tload = [&](bool is_k, uint8_t* tile, int t) __attribute__((always_inline)) {
+  auto tload_w = [&](u32x4 words, uint8_t* tile, int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int blk = (wave & 3) * LPW + j;
@@ -210,8 +229,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
       const int c = lpc ^ swz<D>(row);
       const uint32_t m0 =
           __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(tile - smem) + blk * 1024);
-      dma16<0>(is_k ? wk : wv, m0, (uint32_t)(t * kBK + row) * rstride + c * 16);
+      dma16<0>(words, m0, (uint32_t)(t * kBK + row) * rstride + c * 16);
     }
+  };
+  // K or V resource words of item j of the stream form
+  auto item_words = [&](int j, bool is_k) __attribute__((always_inline)) {
+    int jqb, jh, jbs;
+    stream_item(j, jqb, jh, jbs);
+    return rsrc_words((is_k ? a.k : a.v) + ((long)jbs * a.N * a.H + jh) * D, nbytes);
   };
 
   // ---- per-lane LDS byte offsets of the operand reads (swizzle folded in; the 32-key block,
@@ -354,10 +379,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   // reading in X(t-1). It waits for them at the end of Y(t), before the barrier that precedes
   // their first reader X(t+1). The vector phases, which set the pace, issue no loads (issued
   // there, the loads lengthened them by a fifth).
+  // Position of the next K tile (stream tile t + 1) and V tile (stream tile t) to load: item
+  // and tile within it, with that item's resource words; advanced one tile per load.
+  int kl_j = STREAM ? 1 / ntiles : 0, kl_t = STREAM ? 1 - kl_j * ntiles : 1;
+  int vl_j = 0, vl_t = 0;
+  u32x4 kl_w = wk, vl_w = wv;
+  if (STREAM && kl_j > 0 && kl_j < nitems) kl_w = item_words(kl_j, true);
+  auto advance = [&](int& lj, int& lt, u32x4& lw, bool is_k) __attribute__((always_inline)) {
+    ++lt;
+    if (STREAM && lt == ntiles) {
+      lt = 0;
+      if (++lj < nitems) lw = item_words(lj, is_k);
+    }
+  };
   auto issue = [&](int t) __attribute__((always_inline)) {
     if (grp == 0) {
-      if (t + 1 < ntiles) tload(true, ((t + 1) & 1) ? Ks1 : Ks0, t + 1);
-      if (t < ntiles) tload(false, (t & 1) ? Vs1 : Vs0, t);
+      if (t + 1 < nstream) {
+        tload_w(kl_w, ((t + 1) & 1) ? Ks1 : Ks0, kl_t);
+        advance(kl_j, kl_t, kl_w, true);
+      }
+      if (t < nstream) {
+        tload_w(vl_w, (t & 1) ? Vs1 : Vs0, vl_t);
+        advance(vl_j, vl_t, vl_w, false);
+      }
     }
   };
   auto land = [&]() __attribute__((always_inline)) {
@@ -377,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   // Phase p: group A runs X(p/2) for even p and Y(p/2) for odd p, group B one phase later.
   // A wave's own tiles end at nt_w; it then passes the remaining barriers idle (group A
   // still issuing its share of the loads).
-  if (grp == 0) tload(true, Ks0, 0);
+  if (grp == 0) tload_w(wk, Ks0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   phase_barrier();
   if (grp == 1) phase_barrier();
@@ -385,40 +429,98 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   xphase(I0{}, I1{});
   pin_s();
   phase_barrier();
+  if (STREAM && ntiles == 1 && nitems > 1) {  // item 0's only S is done: Q of item 1
+    int jqb, jh, jbs;
+    stream_item(1, jqb, jh, jbs);
+    load_q(((long)jbs * a.N * a.H + jh) * D, jqb * BQ + rb * 32 + l32);
+  }
   yphase(0);
   pin_p();
   land();
   phase_barrier();
-  int t = 1;
+  // ---- epilogue of an item: O = v_descale * acc / l in bf16 (rows >= L dropped by the
+  // bounds), LSE
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    const float l = lacc[0];
+    const float inv = l > 0.f ? a.v_descale / l : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x16& o = oacc[db];
+        u32x2 v = {pack2<BF16>(o[4 * rr] * inv, o[4 * rr + 1] * inv),
+                   pack2<BF16>(o[4 * rr + 2] * inv, o[4 * rr + 3] * inv)};
+        buf_store8(ro, (uint32_t)qi * (2 * rstride) + (db * 32 + 8 * rr + 4 * g) * 2, v);
+      }
+    if (g == 0 && qi < L) lse[qi] = l > 0.f ? (mref + log2f_hw(l)) * kLn2 : kNegInf;
+  };
+  if constexpr (STREAM) {
+    // stream step gs computes S of tile tin of item j (after the boundary, tile 0 of the
+    // next item) and P V of the stream's previous tile
+    int j = 0, tin = 1;
 #pragma unroll 1
-  for (; t < nt_w; ++t) step(t);
-  issue(t);
-  xphase(I1{}, I0{});
-  phase_barrier();
-  for (; t < ntiles; ++t) {
-    land();
-    phase_barrier();
-    issue(t + 1);
-    phase_barrier();
-  }
-  if (grp == 0) {
-    land();
-    phase_barrier();
-  }
-
-  // ---- epilogue: O = v_descale * acc / l in bf16 (rows >= L dropped by the bounds), LSE
-  const float l = lacc[0];
-  const float inv = l > 0.f ? a.v_descale / l : 0.f;
+    for (int gs = 1; gs < nstream; ++gs) {
+      const bool boundary = tin == ntiles;
+      issue(gs);
+      xphase(I1{}, I1{});
+      pin_s();
+      phase_barrier();
+      if (boundary) {
+        // item j is complete (its last P V and row sum ran in this matrix phase)
+        epilogue();
+        ++j;
+        stream_item(j, qb, h, bs);
+        q0 = qb * BQ;
+        base = ((long)bs * a.N * a.H + h) * D;
+        ro = make_rsrc(a.o + base, 2 * nbytes);
+        lse = a.lse + ((long)bs * a.H + h) * a.N;
+        wq0 = q0 + rb * 32;
+        qi = wq0 + l32;
+        mref = kNegInf;
+        lacc = f32x16{};
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const f32x16& o = oacc[db];
-      u32x2 v = {pack2<BF16>(o[4 * rr] * inv, o[4 * rr + 1] * inv),
-                 pack2<BF16>(o[4 * rr + 2] * inv, o[4 * rr + 3] * inv)};
-      buf_store8(ro, (uint32_t)qi * (2 * rstride) + (db * 32 + 8 * rr + 4 * g) * 2, v);
+        for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+        tin = 0;
+      }
+      if (tin == ntiles - 1 && j + 1 < nitems) {
+        // Q is free after this step's S: load the next item's rows
+        int jqb, jh, jbs;
+        stream_item(j + 1, jqb, jh, jbs);
+        load_q(((long)jbs * a.N * a.H + jh) * D, jqb * BQ + rb * 32 + l32);
+      }
+      yphase(tin);
+      pin_p();
+      land();
+      phase_barrier();
+      ++tin;
     }
-  if (g == 0 && qi < L) lse[qi] = l > 0.f ? (mref + log2f_hw(l)) * kLn2 : kNegInf;
+    issue(nstream);
+    xphase(I1{}, I0{});
+    phase_barrier();
+    if (grp == 0) {
+      land();
+      phase_barrier();
+    }
+    epilogue();
+  } else {
+    int t = 1;
+#pragma unroll 1
+    for (; t < nt_w; ++t) step(t);
+    issue(t);
+    xphase(I1{}, I0{});
+    phase_barrier();
+    for (; t < ntiles; ++t) {
+      land();
+      phase_barrier();
+      issue(t + 1);
+      phase_barrier();
+    }
+    if (grp == 0) {
+      land();
+      phase_barrier();
+    }
+    epilogue();
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -427,8 +529,17 @@ hipError_t launch(const Fp8FwdArgs& a, hipStream_t st) {
   const int nqb = (a.N + BQ - 1) / BQ;
   const long total = (long)nqb * a.H * a.B;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(kThreads), 0, st,
-                     a);
+  if constexpr (!CAUSAL) {
+    // one workgroup per CU (a multiple of the 8 XCDs) when there are at least two items each
+    const int ncu = cu_count() / 8 * 8;
+    if (ncu > 0 && total >= 2L * ncu) {
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, true>), dim3((unsigned)ncu), dim3(kThreads),
+                         0, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false>), dim3((unsigned)total), dim3(kThreads),
+                     0, st, a);
   return hipGetLastError();
 }
 

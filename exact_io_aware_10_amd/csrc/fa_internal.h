@@ -4,7 +4,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fa {
+
+// Compute units of the current device (queried once per device; 0 if the query fails).
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // One forward launch. Dense: B batches of N tokens. Varlen: B = number of sequences,
 // N = max_seqlen, T = total tokens, cu = device cu_seqlens.

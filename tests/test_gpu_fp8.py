@@ -54,6 +54,18 @@ def check(codes, descales, o, lse, causal, scale, slices=None, rows=None):
         assert abs(dl.mean()) <= 2.0 ** -8
 
 
+# Unmasked launches with at least two query blocks per CU (512 on MI355X) take the stream
+# form (one workgroup per CU walking its blocks as one tile stream): items of one tile, of
+# two with a ragged last one, 17 blocks of 33 tiles, and d = 64; sampled slices.
+@pytest.mark.parametrize("B,N,H,d", [(32, 100, 16, 128), (32, 200, 16, 64), (2, 4196, 16, 128),
+                                     (4, 2048, 16, 64)])
+def test_fp8_stream(B, N, H, d):
+    codes, ds = inputs.fp8_inputs(B, N, H, d, seed=N + H)
+    o, lse = run(codes, ds, False, None)
+    check(codes, ds, o, lse, False, None,
+          slices=[(0, 0), (B - 1, H - 1), (B // 2, 7), (1, 3)])
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,N,H,d", [(1, 1, 1, 64), (1, 5, 1, 64), (2, 100, 2, 64),
                                      (1, 257, 2, 128), (2, 300, 3, 128), (1, 1000, 1, 128),
