@@ -316,7 +316,7 @@ def decode_main(args):
     print(json.dumps(out))
 
 
-def fp8_cpu_baseline(wl, codes, descales, min_s=10.0, max_slices=16):
+def fp8_cpu_baseline(wl, codes, descales, min_s=10.0, max_slices=64):
     """The fp64 oracle's FP8 forward (widen the e4m3 codes, apply the descales, plain
     definition) on whole (b, h) slices of the benchmark's inputs, for at least min_s
     seconds or max_slices slices; algorithmic TFLOP/s of the forward."""
