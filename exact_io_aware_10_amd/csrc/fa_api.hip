@@ -3,6 +3,9 @@
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <vector>
 
 #include "fa.h"
 #include "fa_decode.h"
@@ -28,6 +31,31 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool dtype_ok(fa_dtype dt) { return dt == FA_F16 || dt == FA_BF16; }
 
 fa_status to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// FA_DEBUG set to anything but "" or "0" turns on the checks that need a device-to-host
+// copy. Read at every call, so a process can switch it.
+bool debug_checks() {
+  const char* e = getenv("FA_DEBUG");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+
+// Debug check of a packed batch's offsets: copies cu_seqlens to the host on the caller's
+// stream (waiting for the stream) and accepts it only if cu[0] = 0, it never decreases and
+// cu[num_seqs] = total_tokens. Lengths above max_seqlen are allowed (they are truncated).
+fa_status check_cu_seqlens(const int32_t* cu, int num_seqs, int total_tokens,
+                           hipStream_t stream) {
+  std::vector<int32_t> h((size_t)num_seqs + 1);
+  if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return FA_ERR_INVALID_ARG;
+  }
+  if (h[0] != 0 || h[num_seqs] != total_tokens) return FA_ERR_INVALID_ARG;
+  for (int s = 0; s < num_seqs; ++s)
+    if (h[s + 1] < h[s]) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
 
 // Shared checks of the scalar arguments. Returns FA_OK when the request is valid.
 fa_status check_common(long B, long N, long H, int d, fa_dtype dt, float scale) {
@@ -202,6 +230,9 @@ FA_EXPORT fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, v
   if ((long)num_seqs * max_seqlen * H == 0 || total_tokens == 0) return FA_OK;
   if (!tensors_ok({q, k, v, o}) || lse == nullptr || ((uintptr_t)lse & 3u))
     return FA_ERR_INVALID_ARG;
+  if (debug_checks() &&
+      (st = check_cu_seqlens(cu_seqlens, num_seqs, total_tokens, stream)) != FA_OK)
+    return st;
   fa::FwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -232,6 +263,9 @@ FA_EXPORT fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, c
   if (!tensors_ok({q, k, v, o, dout, dq, dk, dv, workspace}) || lse == nullptr ||
       ((uintptr_t)lse & 3u))
     return FA_ERR_INVALID_ARG;
+  if (debug_checks() &&
+      (st = check_cu_seqlens(cu_seqlens, num_seqs, total_tokens, stream)) != FA_OK)
+    return st;
   fa::BwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);

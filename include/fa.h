@@ -183,7 +183,10 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
  * Limit: (max_seqlen + 256) * H * d < 2^30. Sequences longer than max_seqlen are treated
  * as truncated to max_seqlen tokens (their later rows are not written). A malformed cu_seqlens gives undefined results
  * (out-of-range rows are clamped by hardware bounds checks, never read or written outside
- * the packed tensors).
+ * the packed tensors). With the environment variable FA_DEBUG set to anything but "" or
+ * "0" (read at every call), the call first copies cu_seqlens to the host on `stream`,
+ * waits for the stream, and returns FA_ERR_INVALID_ARG without launching anything if
+ * cu[0] != 0, cu decreases anywhere or cu[num_seqs] != total_tokens (or the copy fails).
  */
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int32_t* cu_seqlens, int num_seqs, int total_tokens,
@@ -198,7 +201,8 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
  *   dq, dk, dv       : out, [total_tokens, H, d], dtype; rows of tokens outside every
  *                      sequence are not written
  *   workspace        : fa_bwd_workspace_size(1, total_tokens, H, d) bytes, 16-byte aligned
- * Other arguments, limits and errors as fa_fwd_varlen; deterministic like fa_bwd.
+ * Other arguments, limits, errors and the FA_DEBUG check as fa_fwd_varlen; deterministic
+ * like fa_bwd.
  */
 fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -143,3 +143,46 @@ def test_bwd_varlen_workload_sampled():
         print(f"  seq {s} len {b - a} head {h}", flush=True)
         for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
             assert_close(name, g[a:b, h:h + 1][None], r)
+
+
+def test_varlen_debug_checks(monkeypatch):
+    """With FA_DEBUG set, both packed entry points copy cu_seqlens to the host and reject a
+    malformed array (cu[0] != 0, a decrease, or a last entry other than the token count)
+    with FA_ERR_INVALID_ARG before launching anything; a well-formed array gives the same
+    bits as without the check. FA_DEBUG=0 switches the check off again."""
+    import torch
+    lens = [70, 1, 129, 0, 33]
+    cu = inputs.cu_seqlens(lens)
+    T, H, d = int(cu[-1]), 2, 64
+    print(f"[varlen FA_DEBUG] lens={lens} H={H} d={d} bf16 causal", flush=True)
+    bits = [inputs.normal_bits((T, H, d), "bf16", 60 + i) for i in range(4)]
+    q, k, v, do = (to_device(x, "bf16") for x in bits)
+
+    def run(c):
+        o, lse = fa().fa_fwd_varlen(q, k, v, c, max(lens), causal=True)
+        return (o, lse, *fa().fa_bwd_varlen(q, k, v, o, lse, do, c, max(lens), causal=True))
+
+    monkeypatch.delenv("FA_DEBUG", raising=False)
+    want = run(torch.from_numpy(cu).cuda())
+    monkeypatch.setenv("FA_DEBUG", "1")
+    got = run(torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    for w, g in zip(want, got):
+        assert torch.equal(w, g)
+    o, lse = want[0], want[1]
+    bad = [cu.copy() for _ in range(3)]
+    bad[0][0] = 1                      # does not start at 0
+    bad[1][2], bad[1][3] = cu[3], cu[2]  # decreases
+    bad[2][-1] = T - 1                 # does not end at the token count
+    for c in bad:
+        c_d = torch.from_numpy(c).cuda()
+        with pytest.raises(fa().FAError) as e:
+            fa().fa_fwd_varlen(q, k, v, c_d, max(lens), causal=True)
+        assert e.value.code == 1
+        with pytest.raises(fa().FAError) as e:
+            fa().fa_bwd_varlen(q, k, v, o, lse, do, c_d, max(lens), causal=True)
+        assert e.value.code == 1
+    monkeypatch.setenv("FA_DEBUG", "0")
+    again = run(torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    assert all(torch.equal(w, g) for w, g in zip(want, again))
