@@ -25,6 +25,11 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                                     KERNEL from a FETCH_SIZE run and a
                                                     WRITE_SIZE run that both included a
                                                     --copy-calibration MIB copy
+       python bench.py --mfma-summary DB            prints, per kernel, the matrix-core
+                                                    busy fraction from one run with
+                                                    --kernel-trace and the counters
+                                                    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA,
+                                                    GRBM_GUI_ACTIVE
 """
 import argparse
 import json
@@ -225,6 +230,38 @@ def traffic_summary(fetch_db, write_db, kernels, mib):
     print(f"hbm_read_bytes_per_launch: {rd:.0f}")
     print(f"hbm_write_bytes_per_launch: {wr:.0f}")
     print(f"hbm_bytes_per_launch: {rd + wr:.0f}")
+
+
+def mfma_summary(db_path, simds=1024, xcds=8):
+    """Matrix-core use per kernel from one rocprofv3 run that collected the kernel trace and
+    the counters SQ_VALU_MFMA_BUSY_CYCLES (summed over all SIMDs), SQ_INSTS_MFMA and
+    GRBM_GUI_ACTIVE (summed over the XCDs). Per dispatch: MFMA busy cycles per SIMD, active
+    cycles per XCD, the clock they imply over the traced duration, and busy / active. MI355X:
+    256 CUs of 4 SIMDs in 8 XCDs."""
+    import glob
+    import sqlite3
+    busy = _counter_values(db_path, "SQ_VALU_MFMA_BUSY_CYCLES")
+    insts = _counter_values(db_path, "SQ_INSTS_MFMA")
+    act = _counter_values(db_path, "GRBM_GUI_ACTIVE")
+    dbs = (glob.glob(os.path.join(db_path, "**", "*.db"), recursive=True)
+           if os.path.isdir(db_path) else [db_path])
+    dur = {}
+    for db in dbs:
+        for name, d in sqlite3.connect(db).execute("select name, duration from kernels"):
+            dur.setdefault(name, []).append(d)
+    mean = lambda v: sum(v) / len(v)
+    print(f"# source hash: " + ", ".join(f"{k}={kernel_source_hash(k)}" for k in KERNEL_SOURCES))
+    print(f"# {simds} SIMDs, {xcds} XCDs")
+    print(f"{'calls':>5} {'avg_us':>9} {'mfma_insts':>12} {'busy_per_simd':>14} "
+          f"{'active_per_xcd':>15} {'clock_GHz':>9} {'busy/active':>11}  kernel")
+    for name in sorted(busy, key=lambda n: -mean(busy[n])):
+        b = mean(busy[name])
+        if b <= 0 or name not in act or name not in dur:
+            continue
+        a, t = mean(act[name]) / xcds, mean(dur[name])
+        n = mean(insts[name]) if name in insts else float("nan")
+        print(f"{len(busy[name]):>5} {t / 1e3:>9.1f} {n:>12.4g} {b / simds:>14.0f} "
+              f"{a:>15.0f} {a / t:>9.3f} {b / simds / a:>11.3f}  {name[:100]}")
 
 
 def copy_calibration(mib):
@@ -492,6 +529,9 @@ def ring_main(args):
 def main():
     if "--rocprof-summary" in sys.argv:
         rocprof_summary(sys.argv[sys.argv.index("--rocprof-summary") + 1:])
+        return
+    if "--mfma-summary" in sys.argv:
+        mfma_summary(sys.argv[sys.argv.index("--mfma-summary") + 1])
         return
     if "--traffic-summary" in sys.argv:
         i = sys.argv.index("--traffic-summary")
