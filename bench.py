@@ -25,6 +25,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                                     KERNEL from a FETCH_SIZE run and a
                                                     WRITE_SIZE run that both included a
                                                     --copy-calibration MIB copy
+       python bench.py --configs                    prints forward and backward times of
+                                                    the five parity configurations
        python bench.py --mfma-summary DB            prints, per kernel, the matrix-core
                                                     busy fraction from one run with
                                                     --kernel-trace and the counters
@@ -262,6 +264,58 @@ def mfma_summary(db_path, simds=1024, xcds=8):
         n = mean(insts[name]) if name in insts else float("nan")
         print(f"{len(busy[name]):>5} {t / 1e3:>9.1f} {n:>12.4g} {b / simds:>14.0f} "
               f"{a:>15.0f} {a / t:>9.3f} {b / simds / a:>11.3f}  {name[:100]}")
+
+
+def configs_table(iters=50, warmup=10):
+    """The five parity configurations, each forward and backward call timed with HIP events
+    on the current stream: median of `iters` calls after `warmup`. FLOP counts as the
+    benchmark's (4 N^2 d per (b, h) forward, 2.5 times that backward, halved under the mask;
+    sum of L^2 over the sequences when packed). Prints a text table, not the JSON line."""
+    import torch
+    import exact_io_aware_10_amd as fa
+    from exact_io_aware_10_amd import inputs
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+    def median_ms(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    print(f"{'configuration':<68} {'fwd_us':>8} {'fwd_TF/s':>9} {'%peak':>6} {'bwd_us':>8} "
+          f"{'bwd_TF/s':>9} {'fwd+bwd_TF/s':>12}")
+    for name, wl in inputs.WORKLOADS.items():
+        to = lambda x: torch.from_numpy(x.view(np.int16)).view(tdt[wl.dtype]).cuda()
+        bits = inputs.attention_inputs(1 if wl.varlen else wl.B, wl.N, wl.H, wl.d, wl.dtype,
+                                       0, with_dout=True)
+        mask = " causal" if wl.causal else ""
+        if wl.varlen:
+            lens = inputs.varlen_lengths(wl.N, *wl.len_range, 0)
+            cu = torch.from_numpy(inputs.cu_seqlens(lens)).cuda()
+            q, k, v, do = (to(x)[0] for x in bits)
+            ff = 4.0 * wl.H * wl.d * sum(L * L for L in lens) / (2 if wl.causal else 1)
+            fwd = lambda: fa.fa_fwd_varlen(q, k, v, cu, max(lens), causal=wl.causal)
+            o, lse = fwd()
+            bwd = lambda: fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, max(lens), causal=wl.causal)
+            desc = f"packed T={wl.N} ({len(lens)} seqs) H{wl.H} d{wl.d} {wl.dtype}{mask}"
+        else:
+            q, k, v, do = (to(x) for x in bits)
+            ff = fwd_flops(wl.B, wl.N, wl.H, wl.d, wl.causal)
+            fwd = lambda: fa.fa_fwd(q, k, v, causal=wl.causal)
+            o, lse = fwd()
+            bwd = lambda: fa.fa_bwd(q, k, v, o, lse, do, causal=wl.causal)
+            desc = f"B{wl.B} H{wl.H} N{wl.N} d{wl.d} {wl.dtype}{mask}"
+        tf, tb = median_ms(fwd), median_ms(bwd)
+        print(f"{name + ': ' + desc:<68} {tf * 1e3:>8.1f} {ff / tf / 1e9:>9.1f} "
+              f"{100 * ff / tf / 1e9 / PEAK_BF16_TFLOPS:>6.1f} {tb * 1e3:>8.1f} "
+              f"{2.5 * ff / tb / 1e9:>9.1f} {3.5 * ff / (tf + tb) / 1e9:>12.1f}", flush=True)
 
 
 def copy_calibration(mib):
@@ -544,6 +598,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--configs", action="store_true",
+                    help="print a table of the five parity configurations (forward and "
+                         "backward times, TFLOP/s) instead of the JSON line")
     ap.add_argument("--workload", default=WORKLOAD["name"],
                     help="long_seq_fwd_bwd (default), a decode workload (decode_8k, "
                          "decode_128k), an FP8 forward workload (long_seq_fp8, "
@@ -562,6 +619,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+    if args.configs:
+        configs_table()
+        return
     if args.workload in inputs.FP8_WORKLOADS:
         fp8_main(args)
         return
