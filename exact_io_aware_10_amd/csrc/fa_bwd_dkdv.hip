@@ -92,8 +92,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  auto step = [&](auto bsel, int qt) {
+  // MASK: the step may meet the causal mask (the block's first two query tiles, queries
+  // k0 .. k0+127); later tiles lie wholly below the diagonal and take the branch-free body,
+  // which the compiler schedules as one block
+  auto step = [&](auto bsel, auto msel, int qt) {
     constexpr int B = decltype(bsel)::value;
+    constexpr bool MASK = decltype(msel)::value;
     const uint8_t* qs = B ? Qs1 : Qs0;
     const uint8_t* dos = B ? dOs1 : dOs0;
     const float* nl = B ? nl1 : nl0;
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (qt + 1 < qt_end) load_tile(qt + 1, B ? Qs0 : Qs1, B ? dOs0 : dOs1, B ? nl0 : nl1,
                                    B ? nd0 : nd1);
     const int q0 = qt * kTile + qh * 32;  // this wave's 32 queries: q0 .. q0+31
-    const bool active = !CAUSAL || q0 + 31 >= wk0;
+    const bool active = !MASK || q0 + 31 >= wk0;
     if (active) {
       ln.refresh();
       // S (queries x keys) and dP - D (the accumulator starts at -D of each query)
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) p[4 * a4 + j] = exp2f_hw(fmaf(s[4 * a4 + j], c2, l4[j]));
       }
-      if (CAUSAL && q0 < wk0 + 31) {
+      if (MASK && q0 < wk0 + 31) {
         __builtin_amdgcn_sched_barrier(0);  // keep the mask a branch (diagonal tiles only)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -157,9 +161,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   load_tile(qt_begin, Qs0, dOs0, nl0, nd0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int qt = qt_begin; qt < qt_end; qt += 2) {
-    step(std::integral_constant<int, 0>{}, qt);
-    if (qt + 1 < qt_end) step(std::integral_constant<int, 1>{}, qt + 1);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int qt = qt_begin;  // even: k0 is a multiple of 128, so the buffers alternate from Qs0
+  if constexpr (CAUSAL) {
+    step(B0{}, std::true_type{}, qt);
+    if (qt + 1 < qt_end) step(B1{}, std::true_type{}, qt + 1);
+    qt += 2;
+  }
+  for (; qt < qt_end; qt += 2) {
+    step(B0{}, std::false_type{}, qt);
+    if (qt + 1 < qt_end) step(B1{}, std::false_type{}, qt + 1);
   }
 
   // sum the two query halves' partial gradients of each key group through LDS (the tile

@@ -66,8 +66,11 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int ntiles = (kend + kDqTile - 1) / kDqTile;
   const float c2 = a.scale_log2;
 
-  auto step = [&](auto bsel, int t) {
+  // MASK: the step may meet the causal mask (key tiles from q0 on); earlier tiles lie wholly
+  // below the diagonal and take the branch-free body
+  auto step = [&](auto bsel, auto msel, int t) {
     constexpr int B = decltype(bsel)::value;
+    constexpr bool MASK = decltype(msel)::value;
     const uint8_t* ks = B ? Ks1 : Ks0;
     const uint8_t* vs = B ? Vs1 : Vs0;
     if (t + 1 < ntiles) {
@@ -75,9 +78,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       TL::load(rv, B ? Vs0 : Vs1, (t + 1) * kDqTile, rstride, wave, lane);
     }
     const int kt0 = t * kDqTile;
-    const bool active = !CAUSAL || kt0 <= wq0 + 31;
+    const bool active = !MASK || kt0 <= wq0 + 31;
     if (active) {
-      const bool masked = CAUSAL && kt0 + kDqTile - 1 > wq0;
+      const bool masked = MASK && kt0 + kDqTile - 1 > wq0;
       // the tile's 32-key blocks, one after the other
 #pragma unroll
       for (int kb = 0; kb < kDqTile / 32; ++kb) {
@@ -124,9 +127,21 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   TL::load(rv, Vs0, 0, rstride, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // first tile that can meet the mask: even (q0 is a multiple of 256), so the unmasked loop
+  // ends on a whole pair and the buffers keep alternating from Ks0
+  const int tmask = CAUSAL ? q0 / kDqTile : ntiles;
+  int t = 0;
+  for (; t < ntiles && t < tmask; t += 2) {
+    step(B0{}, std::false_type{}, t);
+    if (t + 1 < ntiles) step(B1{}, std::false_type{}, t + 1);
+  }
+  if constexpr (CAUSAL) {
+    for (; t < ntiles; t += 2) {
+      step(B0{}, std::true_type{}, t);
+      if (t + 1 < ntiles) step(B1{}, std::true_type{}, t + 1);
+    }
   }
 
   // dQ = scale * sum dS k  (signed scale)
