@@ -115,8 +115,6 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
           for (int db = 0; db < DB; ++db)
             dqacc[db] = mfma32<T>(ln.tr_frag(ks, kc * 16, db), sf, dqacc[db]);
         }
-        // finish this half before the next one starts (bounds the live registers)
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
