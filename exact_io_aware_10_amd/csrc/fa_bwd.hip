@@ -19,9 +19,11 @@
 //                        are computed with lanes <-> keys, so P and dS leave the accumulators
 //                        in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS; the two
 //                        halves' partial dK, dV are summed through LDS at the end.
-//   3. bwd_dq_kernel   : one workgroup per 128-query block (32 queries per wave; Q and dO
-//                        in registers); streams 64-key tiles of K and V; S^T and dP^T with
-//                        lanes <-> queries feed dQ^T += K^T dS^T.
+//   3. bwd_dq_kernel   : one workgroup of 8 waves per 256-query block (32 queries per wave;
+//                        Q and dO in registers); streams 64-key tiles of K and V; S^T and
+//                        dP^T with lanes <-> queries feed dQ^T += K^T dS^T.
+// Under the causal mask both gradient kernels run the tiles that can meet the diagonal
+// through a masked copy of their step and all others through the branch-free one.
 // Each streamed tile is stored once, row-major, and read both as row fragments
 // (ds_read_b128: operand rows = tile rows) and as transposed fragments
 // (ds_read_b64_tr_b16: operand rows = tile columns; in each group of 16 lanes, lane i names
