@@ -10,8 +10,10 @@
 // Query row i stands at position Nk - Nq + i of the sequence; the causal mask hides keys
 // after it (for Nq = Nk this is the ordinary causal mask).
 //
-// Kernel 1 (decode_kernel): a workgroup is two (d = 128) or four (d = 64) independent waves,
-// one key range each, over one block of 32 query rows of one (b, h). A wave holds the Q rows
+// Kernel 1 for a single query row (decode1_kernel, the decode step proper): one wave per key
+// range on the vector units, loading K and V rows straight into registers (see the kernel).
+// Kernel 1 for several query rows (decode_kernel): a workgroup is two (d = 128) or four
+// (d = 64) independent waves, one key range each, over one block of 32 query rows of one (b, h). A wave holds the Q rows
 // as MFMA B operands and streams its range in 32-key tiles of K and V from HBM straight into
 // its own part of LDS (buffer_load_dwordx4 ... lds into a ring of four buffers, three tiles in
 // flight, issued from inline assembly so that the compiler does not turn its conservative
@@ -19,9 +21,9 @@
 // (the matrix cores have ample headroom at these shapes: the bound is the K/V stream).
 // Tiles use the dual chunk swizzle of the backward kernels, which keeps both the row-fragment
 // reads of K and the transposed reads of V conflict-free.
-// Kernel 2 (combine_kernel): one wave per output row merges the S partials (their row
-// statistics one per lane, their outputs as independent 16-byte loads over lane groups) and
-// writes O and LSE.
+// Kernel 2 (combine_kernel): four waves per output row merge the S partials (their row
+// statistics one per lane, their outputs as independent 16-byte loads over lane groups and
+// waves) and write O and LSE.
 #include "fa_bwd_common.h"
 #include "fa_decode.h"
 
@@ -238,18 +240,177 @@ __global__ __launch_bounds__(64 * Cfg<D>::kWaves, 1) void decode_kernel(DecodeAr
   }
 }
 
-// One wave per output row (b, q, h): merge the S partials. The row statistics of up to 64
-// partials are loaded at once (one per lane) and reduced across the wave; the partial outputs
-// are then read as independent 16-byte loads, lane group j of the wave taking partials
-// s = j, j + 64/LPR, ... over D/4 lanes of four dims each, and the groups' sums are added at
-// the end. (A loop over the partials in one lane waits for one load after another.)
+// fdot2 of two packed pairs of the element type, accumulated in fp32.
+template <class T>
+__device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+  if constexpr (std::is_same_v<T, BF16>)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                           __builtin_bit_cast(bf16x2, y), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y),
+                                  acc, false);
+}
+
+// Sum over each group of N = 8 or 16 consecutive lanes, in every lane of the group: two quad
+// permutations (lanes i^1, i^2), then the mirror within 8 lanes and the mirror within 16
+// (row_half_mirror, row_mirror) each add the other half's (uniform) sum. Vector adds only.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  auto dpp = [](float v, auto ctrl) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                           decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (N == 16) x += dpp(x, std::integral_constant<int, 0x140>{});  // row_mirror
+  return x;
+}
+
+// Kernel 1 for a single query row (Nq = 1, the decode step proper): one wave per (b, h, key
+// range) on the vector units, no LDS. Lane (rg, c) = (lane / CPR, lane % CPR) takes 16-byte
+// chunk c of rows j0 + rg, j0 + rg + RPW, ...: one load instruction brings RPW whole K (or V)
+// rows, straight into registers, and a batch of U instructions per tensor is in flight while
+// the previous batch is reduced. The score of a row is four v_dot2 per lane and a sum over
+// the row's CPR lanes; P is rounded to the element type as in the other kernels, and
+// O += P V is two v_dot2 per pair of dims with the rounded P paired with zero. Each row group
+// keeps its own lazily rescaled (O, m, l); the RPW groups are merged at the end. The matrix
+// cores would use one of their 32 query columns here; the bound is the K/V stream, and
+// without LDS buffers many more waves per CU keep loads in flight.
+template <int D, class T>
+__global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a) {
+  constexpr int CPR = D / 8;      // lanes (16-byte chunks) per row
+  constexpr int RPW = 64 / CPR;   // rows per load instruction
+  constexpr int U = 8;            // load instructions per tensor and batch
+  constexpr int BR = RPW * U;     // rows per batch
+  const int lane = threadIdx.x & 63;
+  const int rg = lane / CPR, c = lane % CPR;
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long)a.B * a.H * a.S) return;
+  const int s = (int)(w % a.S);
+  const int h = (int)((w / a.S) % a.H);
+  const int b = (int)(w / ((long)a.S * a.H));
+  const int j0 = min(s * a.span, a.Nk);
+  const int j1 = min(j0 + a.span, a.Nk);
+  const int nb = (j1 - j0 + BR - 1) / BR;
+
+  const uint32_t rstride = (uint32_t)a.H * D * 2;
+  const auto rq = make_rsrc(a.q + ((long)b * a.H + h) * D, D * 2);
+  const long kvbase = ((long)b * a.Nk * a.H + h) * D;
+  const uint32_t kvbytes = (uint32_t)(a.Nk - 1) * rstride + D * 2;
+  const auto rk = make_rsrc(a.k + kvbase, kvbytes);
+  const auto rv = make_rsrc(a.v + kvbase, kvbytes);
+  const u32x4 qv = buf_load16(rq, c * 16) ^ a.qsign;
+
+  constexpr bool kBf16 = std::is_same_v<T, BF16>;
+  uint32_t ones = kBf16 ? 0x3f803f80u : 0x3c003c00u;
+  asm volatile("" : "+v"(ones));
+  const float c2 = a.scale_log2;
+  float mref = kNegInf, lsum = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+
+  auto load = [&](u32x4 (&kb)[U], u32x4 (&vb)[U], int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t off = (uint32_t)(j0 + i * BR + u * RPW + rg) * rstride + c * 16;
+      kb[u] = buf_load16(rk, off);
+      vb[u] = buf_load16(rv, off);
+    }
+  };
+  auto reduce = [&](const u32x4 (&kb)[U], const u32x4 (&vb)[U], int i)
+                    __attribute__((always_inline)) {
+    float sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = dot2<T>(kb[u][e], qv[e], acc);
+      sv[u] = group_sum<CPR>(acc);
+      if (j0 + i * BR + u * RPW + rg >= j1) sv[u] = kNegInf;  // past the range
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) mx = fmaxf(mx, sv[u]);
+    const float mnew = mx * c2;  // c2 > 0: a group with no row in range keeps -inf
+    const bool need = mnew > mref + kRescaleSlack;
+    if (__any(need)) {
+      const float alpha = need ? exp2f_hw(mref - mnew) : 1.0f;
+      lsum *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] *= alpha;
+      if (need) mref = mnew;
+    }
+    const float mu = mref == kNegInf ? 0.f : mref;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t plo = pack2<T>(exp2f_hw(fmaf(sv[u], c2, -mu)), 0.f);  // (p, 0)
+      const uint32_t phi = plo << 16;                                       // (0, p)
+      lsum = dot2<T>(plo, ones, lsum);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = dot2<T>(vb[u][e], plo, o[2 * e]);
+        o[2 * e + 1] = dot2<T>(vb[u][e], phi, o[2 * e + 1]);
+      }
+    }
+  };
+
+  u32x4 ka[U], va[U], kn[U], vn[U];
+  if (nb > 0) load(ka, va, 0);
+#pragma unroll 1
+  for (int i = 0; i < nb; i += 2) {
+    if (i + 1 < nb) load(kn, vn, i + 1);
+    reduce(ka, va, i);
+    if (i + 1 < nb) {
+      if (i + 2 < nb) load(ka, va, i + 2);
+      reduce(kn, vn, i + 1);
+    }
+  }
+
+  // merge the RPW row groups (lanes c, c + CPR, ... hold the same dims)
+  float m = mref;
+#pragma unroll
+  for (int x = CPR; x < 64; x *= 2) m = fmaxf(m, __shfl_xor(m, x));
+  const float f = m == kNegInf ? 0.f : exp2f_hw(mref - m);
+  lsum *= f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] *= f;
+#pragma unroll
+  for (int x = CPR; x < 64; x *= 2) {
+    lsum += __shfl_xor(lsum, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], x);
+  }
+  const long part = (long)(b * a.H + h) * a.S + s;  // Nq = 1
+  if (rg == 0) {
+    const auto ro = make_rsrc(a.opart + part * D, D * 4);
+    buf_store16(ro, c * 32, u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]),
+                                  __float_as_uint(o[2]), __float_as_uint(o[3])});
+    buf_store16(ro, c * 32 + 16, u32x4{__float_as_uint(o[4]), __float_as_uint(o[5]),
+                                       __float_as_uint(o[6]), __float_as_uint(o[7])});
+  }
+  if (lane == 0) {
+    a.mpart[part] = m;
+    a.lpart[part] = lsum;
+  }
+}
+
+// One workgroup of four waves per output row (b, q, h): merge the S partials. Every wave
+// reduces the row statistics of all partials (one per lane, 64 at a time); the partial
+// outputs are then split over the four waves and read as independent 16-byte loads, lane
+// group j of a wave taking partials s = j, j + 64/LPR, ... of its share over D/4 lanes of four
+// dims each. The groups' sums are added across lanes, the waves' sums through LDS. (One wave
+// per row walking all partials was bound by the latency of its loads at large S.)
 template <int D, class T>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int LPR = D / 4;      // lanes per partial row (four dims each)
-  constexpr int SPW = 64 / LPR;   // partials read side by side
+  constexpr int SPW = 64 / LPR;   // partials read side by side by one wave
+  constexpr int NW = 4;           // waves per row
+  __shared__ f32x4 wsum[NW][LPR];
   const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= (long)a.B * a.H * a.Nq) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long row = blockIdx.x;
   const int qi = row % a.Nq;
   const long bh = row / a.Nq;  // b * H + h
   const int h = bh % a.H, b = bh / a.H;
@@ -274,7 +435,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (m != kNegInf) {
 #pragma unroll 8
-    for (int s = lane / LPR; s < a.S; s += SPW) {
+    for (int s = wave * SPW + lane / LPR; s < a.S; s += NW * SPW) {
       const long p = part0 + (long)s * a.Nq;
       const float ls = a.lpart[p];
       const float wgt = ls > 0.f ? exp2f_hw(a.mpart[p] - m) : 0.f;
@@ -286,6 +447,13 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   for (int x = LPR; x < 64; x <<= 1)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], x);
+  if (lane < LPR) wsum[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  if (lane < LPR) {
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) acc += wsum[w2][lane];
+  }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   if (lane < LPR) {
     uint16_t* o = a.o + (((long)b * a.Nq + qi) * a.H + h) * D + c4;
@@ -298,16 +466,21 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 template <int D, class T, bool CAUSAL>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   constexpr int kWaves = Cfg<D>::kWaves;
-  const long nqb = (a.Nq + 31) / 32;
-  const long G = (a.S + kWaves - 1) / kWaves;
-  const long grid1 = G * nqb * a.H * a.B;
-  hipLaunchKernelGGL((decode_kernel<D, T, CAUSAL>), dim3((unsigned)grid1), dim3(64 * kWaves),
-                     0, st, a);
+  if (a.Nq == 1) {  // query row Nk - 1 sees every key: the mask never applies
+    const long waves = (long)a.B * a.H * a.S;
+    hipLaunchKernelGGL((decode1_kernel<D, T>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       st, a);
+  } else {
+    const long nqb = (a.Nq + 31) / 32;
+    const long G = (a.S + kWaves - 1) / kWaves;
+    const long grid1 = G * nqb * a.H * a.B;
+    hipLaunchKernelGGL((decode_kernel<D, T, CAUSAL>), dim3((unsigned)grid1), dim3(64 * kWaves),
+                       0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long rows = (long)a.B * a.H * a.Nq;
-  hipLaunchKernelGGL((combine_kernel<D, T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
-                     a);
+  hipLaunchKernelGGL((combine_kernel<D, T>), dim3((unsigned)rows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -322,7 +495,13 @@ hipError_t launch_c(const DecodeArgs& a, bool causal, hipStream_t st) {
 int decode_splits(int B, int Nq, int Nk, int H, int d, int requested) {
   const long tiles = (Nk + dec::kTK - 1) / dec::kTK;  // at least one tile per range
   long s = requested;
-  if (s <= 0) {
+  if (s <= 0 && Nq == 1) {
+    // single-row kernel: about one wave per SIMD of a 256-CU part, each streaming a long
+    // range with its own loads in flight (measured best: at decode_8k and decode_128k, 1024
+    // waves beat 512, 2048 and 4096)
+    const long units = (long)B * H;
+    s = (1024 + units - 1) / units;
+  } else if (s <= 0) {
     // about one workgroup per CU of a 256-CU part: long ranges keep each wave's stream of
     // tiles going, which is what the HBM bandwidth needs
     const long units = (long)B * H * ((Nq + 31) / 32);
