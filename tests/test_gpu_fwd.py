@@ -107,6 +107,22 @@ def test_fwd_stream(B, N, H, d, dtype):
         _check_slices(qb, kb, vb, o, lse, dtype, False, [(0, 0), (B - 1, H - 1), (B // 2, 7)])
 
 
+# Causal dense launches of many query blocks (512 to 1200 items, more than the CUs), dealt
+# longest first over whole slices per XCD: ragged four-tile blocks (all slices checked), a head
+# count that does not split evenly over the XCDs (H = 30 at B = 2) and a ragged N at d = 128.
+@pytest.mark.parametrize("B,N,H,d,dtype", [(32, 200, 16, 64, "bf16"), (1, 6400, 32, 64, "bf16"),
+                                           (2, 5000, 30, 128, "bf16")])
+def test_fwd_causal_many_blocks(B, N, H, d, dtype):
+    (qb, kb, vb), o, lse = run_dense(B, N, H, d, dtype, True, seed=N + H + 1)
+    if N <= 256:
+        w = lambda x: oracle.widen(x, dtype)
+        ro, rlse = oracle.fwd(w(qb), w(kb), w(vb), 1 / math.sqrt(d), True)
+        assert_close("O", o, ro)
+        assert_close("LSE", lse, rlse)
+    else:
+        _check_slices(qb, kb, vb, o, lse, dtype, True, [(0, 0), (B - 1, H - 1), (B // 2, 7)])
+
+
 def run_varlen(lens, H, d, dtype, causal, seed, max_seqlen=None):
     import torch
     cu = inputs.cu_seqlens(lens)
