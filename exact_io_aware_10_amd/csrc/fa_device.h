@@ -142,16 +142,17 @@ __device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff
                : "{m0}"(lds_addr), "v"(voff), "s"(rs), "i"(OFF)
                : "memory");
 }
-// As dma16, with a wave-uniform byte offset soff added to every lane's voff (the
-// instruction's scalar offset): loads that differ only by a uniform amount share voff.
-template <int OFF>
-__device__ __forceinline__ void dma16s(u32x4 rs, uint32_t lds_addr, uint32_t voff,
-                                       uint32_t soff) {
-  static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds"
-               :
-               : "{m0}"(lds_addr), "v"(voff), "s"(rs), "s"(soff), "i"(OFF)
-               : "memory");
+// The resource words over [base + off, base + nbytes): the base address moves up by off
+// bytes and the size shrinks by as much (to 0 if off >= nbytes), so a load at vector offset
+// x reads the byte at base + off + x and is bounds-checked against the original end. (The
+// instruction's scalar offset would not do: it is not part of the bounds check.)
+// w and off must be wave-uniform; the words are read back from the first lane so that
+// they stay in scalar registers, where the load instructions take them.
+__device__ __forceinline__ u32x4 rsrc_advance(u32x4 w, uint32_t off) {
+  const uint64_t a = (((uint64_t)(w[1] & 0xffffu) << 32) | w[0]) + off;
+  const uint32_t n = w[2] > off ? w[2] - off : 0u;
+  auto uni = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); };
+  return u32x4{uni((uint32_t)a), uni((uint32_t)(a >> 32) & 0xffffu), uni(n), uni(w[3])};
 }
 // 4 bytes per lane from a buffer into LDS: lane l writes lds_addr + OFF + 4 l.
 template <int OFF>

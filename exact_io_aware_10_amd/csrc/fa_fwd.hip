@@ -199,22 +199,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const int lrow = lane / CPR, lpc = lane % CPR;
   const u32x4 wk = rsrc_words(a.k + base, nbytes), wv = rsrc_words(a.v + base, nbytes);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  // Per-lane part of each load's source offset: the lane's row within its 1 KiB block and its
-  // swizzled chunk (computed once); the block's first row and the tile are a uniform offset
-  // passed as the instruction's scalar offset, so issuing a load takes no vector work.
+  // Per-lane source offset of each load: the lane's row (the block's first row plus the lane's
+  // row within the block) and its swizzled chunk, computed once. The tile's first row moves
+  // the resource's base address and shrinks its size (tile_words), so every row offset stays
+  // in the bounds-checked vector offset: rows past the sequence read as zero, and no load
+  // touches memory past the end of the tensor. Issuing a load takes no vector work.
   uint32_t kof[LPW], vof[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int row = ((wave & 3) * LPW + j) * RPL + lrow;
-    kof[j] = (uint32_t)lrow * rstride + (uint32_t)((lpc ^ kswz<D>(row)) * 16);
-    vof[j] = (uint32_t)lrow * rstride + (uint32_t)((lpc ^ vswz<D>(row)) * 16);
+    kof[j] = (uint32_t)row * rstride + (uint32_t)((lpc ^ kswz<D>(row)) * 16);
+    vof[j] = (uint32_t)row * rstride + (uint32_t)((lpc ^ vswz<D>(row)) * 16);
   }
-  auto tload_one = [&](u32x4 words, bool is_k, uint8_t* tile, int t, int j)
+  auto tload_one = [&](u32x4 words, bool is_k, uint8_t* tile, int j)
       __attribute__((always_inline)) {
     const int blk = (wave & 3) * LPW + j;
     const uint32_t m0 =
         __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(tile - smem) + blk * 1024);
-    dma16s<0>(words, m0, is_k ? kof[j] : vof[j], (uint32_t)(t * kBK + blk * RPL) * rstride);
+    dma16<0>(words, m0, is_k ? kof[j] : vof[j]);
   };
   // buffer resource words of K or V for item j of the stream form
   auto item_words = [&](int j, bool is_k) __attribute__((always_inline)) {
@@ -223,8 +225,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     return rsrc_words((is_k ? a.k : a.v) + ((long)jbs * a.N * a.H + jh) * D, nbytes);
   };
   auto tload_w = [&](u32x4 words, bool is_k, uint8_t* tile, int t) __attribute__((always_inline)) {
+    const u32x4 tw = rsrc_advance(words, (uint32_t)(t * kBK) * rstride);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) tload_one(words, is_k, tile, t, j);
+    for (int j = 0; j < LPW; ++j) tload_one(tw, is_k, tile, j);
   };
   // tile s of the stream (prologue): tile s of this item, or (stream form) tile s % ntiles
   // of item s / ntiles

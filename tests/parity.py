@@ -9,9 +9,12 @@ deviation of about 0.018). The relative check is skipped when the reference's RM
 below 1e-4 (an exactly-zero gradient, e.g. dQ with a single visible key).
 
 Tests at softmax scales other than 1/sqrt(d) (not one of the five workloads) can produce
-gradients of magnitude 10 or more, where rounding the output to bf16 alone costs up to
-half an ulp = 2^-9 |x|; they pass rtol = 2^-7 (two half-ulps), applied elementwise on top
-of the absolute bound.
+gradients of magnitude 8 or more. There rounding the output to bf16 alone can cost more
+than the absolute bound: half an ulp is 2^-5 = 0.031 on [8, 16) (at most 2^-8 |x| in
+general). Those tests pass rtol = 2^-7 (two such half-ulps), which adds rtol * |ref| to the
+absolute bound only for elements with |ref| >= 8; every smaller element is held to the
+plain bound. (Checks of a result that is itself a rounding of the reference, such as the
+rounded copy of a merged fp32 output, pass rtol_from=0.)
 """
 import numpy as np
 
@@ -20,6 +23,8 @@ import oracle
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
 REL_FRO = 1e-2
+# |ref| from which a bf16 output's half-ulp (2^-5 on [8, 16)) exceeds MAX_ABS by itself
+RTOL_FROM = 8.0
 
 
 def torch_dtype(dtype):
@@ -54,17 +59,19 @@ def err_stats(got, ref):
 
 
 def assert_close(name, got, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS, rel_fro=REL_FRO,
-                 rtol=0.0):
+                 rtol=0.0, rtol_from=RTOL_FROM, quiet=False):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     s = err_stats(got, ref)
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    excess = float(np.max(np.abs(got - ref) - rtol * np.abs(ref))) if ref.size else 0.0
-    print(f"  {name}: max_abs={s['max_abs']:.3e} mean_abs={s['mean_abs']:.3e} "
-          f"rel_fro={s['rel_fro']:.3e} ref_rms={rms:.3e} max|ref|="
-          f"{float(np.max(np.abs(ref))) if ref.size else 0:.3e}", flush=True)
+    slack = rtol * np.where(np.abs(ref) >= rtol_from, np.abs(ref), 0.0)
+    excess = float(np.max(np.abs(got - ref) - slack)) if ref.size else 0.0
+    if not quiet:
+        print(f"  {name}: max_abs={s['max_abs']:.3e} mean_abs={s['mean_abs']:.3e} "
+              f"rel_fro={s['rel_fro']:.3e} ref_rms={rms:.3e} max|ref|="
+              f"{float(np.max(np.abs(ref))) if ref.size else 0:.3e}", flush=True)
     assert excess <= max_abs, (name, s, excess)
     assert s["mean_abs"] <= mean_abs, (name, s)
     if rms >= 1e-4:
