@@ -77,37 +77,51 @@ def bwd_flops(B, N, H, d, causal):
     return f / 2 if causal else f
 
 
-def cpu_baseline(wl, bits, min_s=10.0, max_slices=16):
-    """The fp64 oracle timed on the host on a bounded sample of the same workload: whole
-    (b, h) slices of the benchmark's own inputs at full length (forward + backward of each
-    slice is one complete attention problem), repeated until at least `min_s` seconds of
-    host time or `max_slices` slices. Reported as algorithmic TFLOP/s (same FLOP count as
-    the GPU metric)."""
+def host_cores():
+    """(threads the oracle uses, CPUs this process may run on, CPUs of the host)."""
+    import oracle
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count() or 1
+    return oracle.default_threads(), aff, os.cpu_count() or aff
+
+
+def cpu_baseline(wl, bits, bwd_slices=4):
+    """The fp64 oracle timed on the host on the same workload: the forward of every (b, h)
+    slice of the benchmark's inputs (the whole forward), then forward + backward of the first
+    `bwd_slices` slices (each one complete attention problem). Reported as algorithmic
+    TFLOP/s of that sample (same FLOP counts as the GPU metric)."""
     import oracle
 
     d, dtype, causal, N = wl["d"], wl["dtype"], wl["causal"], wl["N"]
     scale = 1 / math.sqrt(d)
-    nth = oracle.default_threads()
+    nth, aff, ncpu = host_cores()
     w = lambda x: oracle.widen(x, dtype)
     B, H = wl["B"], wl["H"]
-    slices = [(b, h) for b in range(B) for h in range(H)]
-    done = 0
+    t0 = time.perf_counter()
+    q, k, v = (w(x) for x in bits[:3])
+    oracle.fwd(q, k, v, scale, causal, nthreads=nth)
+    fwd_s = time.perf_counter() - t0
+    del q, k, v
     secs = 0.0
-    for b, h in slices[:max_slices]:
+    for b, h in [(b, h) for b in range(B) for h in range(H)][:bwd_slices]:
         q, k, v, do = (w(np.ascontiguousarray(x[b:b + 1, :, h:h + 1, :])) for x in bits)
         t0 = time.perf_counter()
         o, lse = oracle.fwd(q, k, v, scale, causal, nthreads=nth)
         oracle.bwd(q, k, v, o, lse, do, scale, causal, nthreads=nth)
         secs += time.perf_counter() - t0
-        done += 1
-        if secs >= min_s:
-            break
-    flops = done * (fwd_flops(1, N, 1, d, causal) + bwd_flops(1, N, 1, d, causal))
-    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": nth,
-            "kind": "oracle",
-            "sample": f"fp64 oracle forward + backward of {done} of the {B * H} (b,h) slices "
-                      f"of the benchmark's inputs (N={N}, d={d}), {secs:.1f} s on {nth} "
-                      f"host threads"}
+    flops = (fwd_flops(B, N, H, d, causal)
+             + bwd_slices * (fwd_flops(1, N, 1, d, causal) + bwd_flops(1, N, 1, d, causal)))
+    return {"value": round(flops / (fwd_s + secs) / 1e12, 6), "unit": "TFLOP/s",
+            "cores": nth, "kind": "oracle",
+            "fwd_tflops": round(fwd_flops(B, N, H, d, causal) / fwd_s / 1e12, 6),
+            "host_cpus_allowed": aff, "host_cpus": ncpu,
+            "sample": f"fp64 oracle forward of all {B * H} (b,h) slices of the benchmark's "
+                      f"inputs (N={N}, d={d}; {fwd_s:.1f} s), then forward + backward of "
+                      f"{bwd_slices} slices ({secs:.1f} s), on {nth} host threads (the "
+                      f"process may run on {aff} of the host's {ncpu} CPUs; the thread "
+                      f"count is the GPU's share of them, OMP_NUM_THREADS, or at most 16)"}
 
 
 def kernel_source_hash(kernel):
@@ -144,6 +158,29 @@ def measured_traffic_for(stem, kernel):
         return int(float(vals["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def measured_mfma_busy(kernel, stem="long_seq"):
+    """Share of the dispatch's cycles in which a SIMD's matrix core is busy, for `kernel`,
+    from the committed rocprofv3 counter summary profiles/mfma_busy_<stem>.txt (its
+    busy/active column), or None when that summary is missing or was taken on other kernel
+    source than the current one."""
+    path = os.path.join(ROOT, "profiles", f"mfma_busy_{stem}.txt")
+    if not os.path.exists(path):
+        return None
+    want = kernel_source_hash(kernel)
+    ok = False
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if line.startswith("# source hash:"):
+                ok = f"{kernel}={want}" in line
+            elif ok and not line.startswith("#") and f"{kernel}<" in line:
+                cols = line.split()
+                try:
+                    return float(cols[6])
+                except (IndexError, ValueError):
+                    return None
+    return None
 
 
 def rocprof_summary(paths):
@@ -704,6 +741,13 @@ def main():
         per_kernel[name] = {"ms": round(t, 4), "bound": bound,
                             ("tflops" if bound == "mfma" else "gbps"):
                                 round(rate / (1e12 if bound == "mfma" else 1e9), 2)}
+    for name in per_kernel:
+        busy = measured_mfma_busy(name)
+        traffic = measured_traffic(name)
+        per_kernel[name]["mfma_busy"] = busy
+        per_kernel[name]["hbm_bytes"] = traffic
+        per_kernel[name]["hbm_gbps"] = (round(traffic / (kms[name] * 1e-3) / 1e9, 1)
+                                        if traffic else None)
     dom = max(kms, key=kms.get)
     bound, amount = work[dom]
     if bound == "mfma":
@@ -727,6 +771,11 @@ def main():
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_pct_of_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "kernels": per_kernel,
+        "kernel_counters": "mfma_busy: matrix-core busy share of each kernel's cycles "
+                           "(profiles/mfma_busy_long_seq.txt); hbm_bytes: HBM bytes per "
+                           "launch (profiles/<kernel>_long_seq_traffic.txt), hbm_gbps = "
+                           "hbm_bytes / this run's launch time; null where the committed "
+                           "counters were taken on other kernel source",
         "wall_s": round(wall, 3),
         "roofline": roofline,
     }

@@ -28,7 +28,8 @@ __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fw
            "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libfa_mi355x.so")
+# FA_LIBRARY selects another build of the same library (the debug variants of build.py)
+library_path = os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa_mi355x.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F16, FA_BF16 = 0, 1

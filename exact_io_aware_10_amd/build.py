@@ -2,9 +2,17 @@
 
 Every .hip file under csrc/ is compiled to an object in parallel, then linked into
 exact_io_aware_10_amd/libfa_mi355x.so. Usage: python -m exact_io_aware_10_amd.build [-v]
+[--variant lds_poison|host_asan]
 
 Environment (optional): FA_EXTRA_CFLAGS (extra hipcc flags for every file), FA_LIB_OUT
 (output library path), FA_BUILD_DIR (object directory).
+
+Debug variants (build_variant), each its own library under exact_io_aware_10_amd/variants/,
+loaded by setting FA_LIBRARY to its path:
+  lds_poison  every kernel fills its LDS with NaN patterns before use (-DFA_LDS_POISON)
+  host_asan   host code built with AddressSanitizer and UndefinedBehaviorSanitizer (the
+              argument checks of the C ABI; device code unchanged), for a process that
+              preloads clang's ASan runtime
 """
 import os
 import subprocess
@@ -44,9 +52,10 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _compile(src, verbose, build_dir=BUILD_DIR, extra=()):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o",
+           obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -68,5 +77,41 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+VARIANTS = {
+    "lds_poison": (["-DFA_LDS_POISON"], []),
+    "host_asan": (["-Xarch_host", "-fsanitize=address",
+                   "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-omit-frame-pointer", "-g"],
+                  ["-Xarch_host", "-fsanitize=address",
+                   "-Xarch_host", "-fsanitize=undefined"]),
+}
+VARIANT_DIR = os.path.join(HERE, "variants")
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(VARIANT_DIR, f"libfa_mi355x_{name}.so")
+
+
+def build_variant(name: str, verbose: bool = False, jobs: int = 8) -> str:
+    """Build the debug variant `name` of the library (see the module docstring)."""
+    cflags, ldflags = VARIANTS[name]
+    bdir = os.path.join(BUILD_DIR, name)
+    os.makedirs(bdir, exist_ok=True)
+    os.makedirs(VARIANT_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, bdir, cflags), sources()))
+    out = variant_path(name)
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *ldflags, *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--variant" in sys.argv:
+        print(build_variant(sys.argv[sys.argv.index("--variant") + 1], verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

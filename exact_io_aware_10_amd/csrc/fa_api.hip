@@ -28,7 +28,7 @@ float exp_scale(float softmax_scale) { return fmaxf(fabsf(softmax_scale) * kLog2
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool dtype_ok(fa_dtype dt) { return dt == FA_F16 || dt == FA_BF16; }
+bool dtype_ok(int dt) { return dt == FA_F16 || dt == FA_BF16; }
 
 fa_status to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
@@ -58,7 +58,7 @@ fa_status check_cu_seqlens(const int32_t* cu, int num_seqs, int total_tokens,
 }
 
 // Shared checks of the scalar arguments. Returns FA_OK when the request is valid.
-fa_status check_common(long B, long N, long H, int d, fa_dtype dt, float scale) {
+fa_status check_common(long B, long N, long H, int d, int dt, float scale) {
   if (B < 0 || N < 0 || H < 0) return FA_ERR_INVALID_ARG;
   if (!dtype_ok(dt) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -75,8 +75,8 @@ bool tensors_ok(std::initializer_list<const void*> ps) {
 
 }  // namespace
 
-FA_EXPORT const char* fa_status_string(fa_status s) {
-  switch (s) {
+FA_EXPORT const char* fa_status_string(int status) {
+  switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration";
@@ -86,7 +86,7 @@ FA_EXPORT const char* fa_status_string(fa_status s) {
 }
 
 FA_EXPORT fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int N, int H, int d, fa_dtype dtype, float softmax_scale,
+                           int B, int N, int H, int d, int dtype, float softmax_scale,
                            int causal, hipStream_t stream) {
   fa_status st = check_common(B, N, H, d, dtype, softmax_scale);
   if (st != FA_OK) return st;
@@ -141,7 +141,7 @@ FA_EXPORT fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void
 
 FA_EXPORT fa_status fa_merge(float* o_acc, float* lse_acc, const void* o_part,
                              const float* lse_part, void* out, int B, int N, int H, int d,
-                             fa_dtype dtype, hipStream_t stream) {
+                             int dtype, hipStream_t stream) {
   fa_status st = check_common(B, N, H, d, dtype, 1.0f);
   if (st != FA_OK) return st;
   if ((long)B * N * H == 0) return FA_OK;
@@ -170,7 +170,7 @@ namespace {
 
 fa_status bwd_common(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                     void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                     void* workspace, int B, int N, int H, int d, int dtype,
                      float softmax_scale, int causal, int stage, hipStream_t stream) {
   fa_status st = check_common(B, N, H, d, dtype, softmax_scale);
   if (st != FA_OK) return st;
@@ -207,7 +207,7 @@ fa_status bwd_common(const void* q, const void* k, const void* v, const void* o,
   FA_EXPORT fa_status name(const void* q, const void* k, const void* v, const void* o,    \
                            const float* lse, const void* dout, void* dq, void* dk,        \
                            void* dv, void* workspace, int B, int N, int H, int d,         \
-                           fa_dtype dtype, float softmax_scale, int causal,               \
+                           int dtype, float softmax_scale, int causal,               \
                            hipStream_t stream) {                                          \
     return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, N, H, d, dtype,    \
                       softmax_scale, causal, stage, stream);                              \
@@ -221,7 +221,7 @@ FA_BWD_ENTRY(fa_bwd_dq, fa::kBwdDq)
 FA_EXPORT fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                                   float* lse, const int32_t* cu_seqlens, int num_seqs,
                                   int total_tokens, int max_seqlen, int H, int d,
-                                  fa_dtype dtype, float softmax_scale, int causal,
+                                  int dtype, float softmax_scale, int causal,
                                   hipStream_t stream) {
   if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0) return FA_ERR_INVALID_ARG;
   fa_status st = check_common(num_seqs, max_seqlen, H, d, dtype, softmax_scale);
@@ -253,7 +253,7 @@ FA_EXPORT fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, c
                                   const float* lse, const void* dout, void* dq, void* dk,
                                   void* dv, void* workspace, const int32_t* cu_seqlens,
                                   int num_seqs, int total_tokens, int max_seqlen, int H, int d,
-                                  fa_dtype dtype, float softmax_scale, int causal,
+                                  int dtype, float softmax_scale, int causal,
                                   hipStream_t stream) {
   if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0) return FA_ERR_INVALID_ARG;
   fa_status st = check_common(num_seqs, max_seqlen, H, d, dtype, softmax_scale);
@@ -317,7 +317,7 @@ FA_EXPORT size_t fa_fwd_splitkv_workspace_size(int B, int Nq, int Nk, int H, int
 
 FA_EXPORT fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
                                    float* lse, void* workspace, int B, int Nq, int Nk, int H,
-                                   int d, fa_dtype dtype, float softmax_scale, int causal,
+                                   int d, int dtype, float softmax_scale, int causal,
                                    int num_splits, hipStream_t stream) {
   fa_status st = splitkv_sizes(B, Nq, Nk, H, d, num_splits);
   if (st != FA_OK) return st;

@@ -31,6 +31,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(256))) float nl1[kTile];
   __shared__ __attribute__((aligned(256))) float nd0[kTile];  // -D
   __shared__ __attribute__((aligned(256))) float nd1[kTile];
+  for (void* p : {(void*)Qs0, (void*)Qs1, (void*)dOs0, (void*)dOs1, (void*)Vk0, (void*)Vk1})
+    lds_poison(p, TL::BYTES);
+  for (float* p : {nl0, nl1, nd0, nd1}) lds_poison(p, kTile * 4);
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;

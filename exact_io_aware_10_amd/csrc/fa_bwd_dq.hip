@@ -25,6 +25,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t Ks1[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t Vs0[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t Vs1[TL::BYTES];
+  for (void* p : {(void*)Ks0, (void*)Ks1, (void*)Vs0, (void*)Vs1}) lds_poison(p, TL::BYTES);
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;

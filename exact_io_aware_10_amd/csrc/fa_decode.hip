@@ -73,6 +73,8 @@ __global__ __launch_bounds__(64 * Cfg<D>::kWaves, 1) void decode_kernel(DecodeAr
   // per wave: kBufs buffers of a K tile and a V tile
   constexpr int WAVEB = kBufs * 2 * TB;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * WAVEB];
+  lds_poison(smem, sizeof(smem));
+  lds_poison_done();
 
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -408,6 +410,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int SPW = 64 / LPR;   // partials read side by side by one wave
   constexpr int NW = 4;           // waves per row
   __shared__ f32x4 wsum[NW][LPR];
+  lds_poison(wsum, sizeof(wsum));
+  lds_poison_done();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const long row = blockIdx.x;

@@ -175,6 +175,25 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Debug builds compiled with -DFA_LDS_POISON: every kernel first fills the LDS it declares
+// with all-ones words (NaN as bf16, fp16 and fp32 data, 0xFF as e4m3: NaN), then passes a
+// workgroup barrier, so an operand read from LDS that no load or store wrote shows up as
+// NaN in the outputs. Without the macro both calls compile to nothing.
+__device__ __forceinline__ void lds_poison(void* p, int bytes) {
+#ifdef FA_LDS_POISON
+  uint32_t* w = reinterpret_cast<uint32_t*>(p);
+  for (int i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0xffffffffu;
+#else
+  (void)p;
+  (void)bytes;
+#endif
+}
+__device__ __forceinline__ void lds_poison_done() {
+#ifdef FA_LDS_POISON
+  __syncthreads();
+#endif
+}
+
 // Workgroup barrier between phases that share LDS: waits for this wave's LDS accesses
 // (lgkmcnt) but not for its outstanding buffer -> LDS loads. __syncthreads() would also wait
 // for those (vmcnt 0), i.e. for every prefetch meant to stay in flight across the barrier;

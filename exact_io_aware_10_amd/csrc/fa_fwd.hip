@@ -114,6 +114,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // (three, so that a K tile can be loaded while both groups are still reading the two
   // before it). 160 KiB at d = 128.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * TILEB];
+  lds_poison(smem, sizeof(smem));
+  lds_poison_done();
   auto kbuf = [&](int i) __attribute__((always_inline)) { return smem + (2 + i) * TILEB; };
   auto vbuf = [&](int i) __attribute__((always_inline)) { return smem + i * TILEB; };
 

@@ -147,6 +147,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_fp8_kernel(Fp8FwdArgs a) {
   // four tile buffers: K at 0 and TILEB, V at 2 TILEB and 3 TILEB; switching buffers is an
   // XOR of bit log2(TILEB) of the per-lane offsets
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];
+  lds_poison(smem, sizeof(smem));
+  lds_poison_done();
   uint8_t* const Ks0 = smem;
   uint8_t* const Ks1 = smem + TILEB;
   uint8_t* const Vs0 = smem + 2 * TILEB;

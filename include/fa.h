@@ -52,10 +52,13 @@ typedef enum {
   FA_ERR_HIP = 3          /* a HIP launch reported an error */
 } fa_status;
 
+/* Element type codes, passed as the int argument dtype (any other value is rejected with
+ * FA_ERR_INVALID_ARG). */
 typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 
-/* Short static description of a status code. Never NULL. */
-const char* fa_status_string(fa_status s);
+/* Short static description of a status code (an fa_status value; any other int gives
+ * "unknown status"). Never NULL. */
+const char* fa_status_string(int status);
 
 /*
  * Forward pass (guide §6.2 tiled algorithm; narration 第二招 for the deferred
@@ -67,7 +70,7 @@ const char* fa_status_string(fa_status s);
  * B, N, H >= 0 (B*N*H == 0 is a no-op returning FA_OK). Limit: (N + 256) * H * d < 2^30.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                 int N, int H, int d, fa_dtype dtype, float softmax_scale, int causal,
+                 int N, int H, int d, int dtype, float softmax_scale, int causal,
                  hipStream_t stream);
 
 /*
@@ -116,7 +119,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
  * dV and its share of dQ (the shares of dQ add up).
  */
 fa_status fa_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part,
-                   void* out, int B, int N, int H, int d, fa_dtype dtype, hipStream_t stream);
+                   void* out, int B, int N, int H, int d, int dtype, hipStream_t stream);
 
 /*
  * Bytes of device workspace fa_bwd needs: 8 * B * H * N (two fp32 row terms per query:
@@ -142,7 +145,7 @@ size_t fa_bwd_workspace_size(int B, int N, int H, int d);
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                 void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                 void* workspace, int B, int N, int H, int d, int dtype,
                  float softmax_scale, int causal, hipStream_t stream);
 
 /*
@@ -157,15 +160,15 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
  */
 fa_status fa_bwd_prep(const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                      void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                      void* workspace, int B, int N, int H, int d, int dtype,
                       float softmax_scale, int causal, hipStream_t stream);
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                      void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                      void* workspace, int B, int N, int H, int d, int dtype,
                       float softmax_scale, int causal, hipStream_t stream);
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                    void* workspace, int B, int N, int H, int d, fa_dtype dtype,
+                    void* workspace, int B, int N, int H, int d, int dtype,
                     float softmax_scale, int causal, hipStream_t stream);
 
 /*
@@ -190,7 +193,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
  */
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int32_t* cu_seqlens, int num_seqs, int total_tokens,
-                        int max_seqlen, int H, int d, fa_dtype dtype, float softmax_scale,
+                        int max_seqlen, int H, int d, int dtype, float softmax_scale,
                         int causal, hipStream_t stream);
 
 /*
@@ -207,7 +210,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
 fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
                         void* workspace, const int32_t* cu_seqlens, int num_seqs,
-                        int total_tokens, int max_seqlen, int H, int d, fa_dtype dtype,
+                        int total_tokens, int max_seqlen, int H, int d, int dtype,
                         float softmax_scale, int causal, hipStream_t stream);
 
 /*
@@ -235,7 +238,7 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  */
 size_t fa_fwd_splitkv_workspace_size(int B, int Nq, int Nk, int H, int d, int num_splits);
 fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                         void* workspace, int B, int Nq, int Nk, int H, int d, fa_dtype dtype,
+                         void* workspace, int B, int Nq, int Nk, int H, int d, int dtype,
                          float softmax_scale, int causal, int num_splits, hipStream_t stream);
 
 #ifdef __cplusplus

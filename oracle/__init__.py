@@ -57,12 +57,19 @@ def _load():
 
 
 def default_threads() -> int:
-    """Host threads for the oracle: the cores this process may run on, at most 16."""
+    """Host threads for the oracle: the CPUs this process may run on (its affinity), at most
+    OMP_NUM_THREADS where that is set (a GPU host's share of its CPUs per GPU), else at most
+    16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    cap = 16
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "") or 16)
+    except ValueError:
+        pass
+    return max(1, min(n, cap))
 
 
 def widen(bits: np.ndarray, dtype: str) -> np.ndarray:

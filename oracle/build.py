@@ -22,6 +22,23 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_LIB = os.path.join(HERE, "liboracle_asan.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer build for the sanitizer test (host code
+# only; loaded with gcc's sanitizer runtimes preloaded)
+ASAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", "-shared", "-fPIC",
+              "-pthread", "-Wall"]
+
+
+def build_asan(verbose: bool = False) -> str:
+    tmp = ASAN_LIB + ".tmp"
+    cmd = ["g++", *ASAN_FLAGS, "-fsanitize=address,undefined", SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 def build_from_text(source_text: str, out_path: str) -> str:
     """Compile a (modified) copy of the oracle source to out_path; used by the mutation test."""
     src = out_path + ".cpp"

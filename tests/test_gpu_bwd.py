@@ -54,7 +54,7 @@ def test_bwd_scale_values(scale):
         bits, got = run(1, 150, 2, 64, "bf16", causal, seed=5, scale=scale)
         ref = oracle_grads(bits, "bf16", scale, causal)
         for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-            assert_close(name, g, r, rtol=2.0 ** -7)
+            assert_close(name, g, r, ulps=1)
 
 
 def test_bwd_deterministic():
@@ -127,8 +127,11 @@ def test_bwd_varlen_small(d, causal):
     scale = 1 / math.sqrt(d)
     o, lse = oracle.fwd_varlen(q, k, v, cu, scale, causal)
     ref = oracle.bwd_varlen(q, k, v, o, lse, do, cu, scale, causal)
+    # short causal sequences (lengths 1, 5, 17) give gradients of magnitude 4 and more, where
+    # the bf16 output's own rounding costs up to 2^-6 = 0.0156 of the 2e-2 bound: one
+    # half-ulp of the output is added to the bound (parity.py)
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        assert_close(name, g, r)
+        assert_close(name, g, r, ulps=1)
 
 
 def test_bwd_varlen_workload():

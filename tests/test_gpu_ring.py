@@ -56,7 +56,7 @@ def test_merge_against_oracle(d, dtype):
     np.testing.assert_allclose(got_o, ro, rtol=2e-6, atol=2e-6)
     # the rounded copy: within half an ulp of the element type (2^-9 relative for bf16)
     assert_close("out", f64_of(out, dtype), ro, max_abs=1e-6, mean_abs=1e-2, rel_fro=1e-2,
-                 rtol=2.0 ** -8, rtol_from=0.0)
+                 rtol=2.0 ** -8)
 
 
 def ring(B, N, H, d, dtype, causal, P, seed, backward):
@@ -125,4 +125,4 @@ def test_ring_backward(causal):
     rq, rk, rv = oracle.bwd(w[0], w[1], w[2], ro, rl, w[3], scale, causal)
     # each chunk's share is rounded to bf16 before the shares are added: up to P roundings
     for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv)):
-        assert_close(name, g, r, rtol=P * 2.0 ** -9, rtol_from=0.0)
+        assert_close(name, g, r, rtol=P * 2.0 ** -9)
