@@ -7,8 +7,9 @@ exact_io_aware_10_amd/libfa_mi355x.so. Usage: python -m exact_io_aware_10_amd.bu
 Environment (optional): FA_EXTRA_CFLAGS (extra hipcc flags for every file), FA_LIB_OUT
 (output library path), FA_BUILD_DIR (object directory).
 
-Debug variants (build_variant), each its own library under exact_io_aware_10_amd/variants/,
-loaded by setting FA_LIBRARY to its path:
+Debug variants (build_variant), each its own library (variant_path: under
+exact_io_aware_10_amd/variants/, the sanitizer build under the object directory), loaded by
+setting FA_LIBRARY to its path:
   lds_poison  every kernel fills its LDS with NaN patterns before use (-DFA_LDS_POISON)
   host_asan   host code built with AddressSanitizer and UndefinedBehaviorSanitizer (the
               argument checks of the C ABI; device code unchanged), for a process that
@@ -89,7 +90,9 @@ VARIANT_DIR = os.path.join(HERE, "variants")
 
 
 def variant_path(name: str) -> str:
-    return os.path.join(VARIANT_DIR, f"libfa_mi355x_{name}.so")
+    # the sanitizer build serves CPU tests only and stays with the objects
+    d = os.path.join(BUILD_DIR, name) if name == "host_asan" else VARIANT_DIR
+    return os.path.join(d, f"libfa_mi355x_{name}.so")
 
 
 def build_variant(name: str, verbose: bool = False, jobs: int = 8) -> str:
@@ -97,7 +100,7 @@ def build_variant(name: str, verbose: bool = False, jobs: int = 8) -> str:
     cflags, ldflags = VARIANTS[name]
     bdir = os.path.join(BUILD_DIR, name)
     os.makedirs(bdir, exist_ok=True)
-    os.makedirs(VARIANT_DIR, exist_ok=True)
+    os.makedirs(os.path.dirname(variant_path(name)), exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, bdir, cflags), sources()))
     out = variant_path(name)

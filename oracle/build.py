@@ -22,7 +22,7 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-ASAN_LIB = os.path.join(HERE, "liboracle_asan.so")
+ASAN_LIB = os.path.join(os.path.dirname(HERE), "_build", "asan", "liboracle_asan.so")
 # AddressSanitizer and UndefinedBehaviorSanitizer build for the sanitizer test (host code
 # only; loaded with gcc's sanitizer runtimes preloaded)
 ASAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", "-shared", "-fPIC",
@@ -30,6 +30,7 @@ ASAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", "-shared", "
 
 
 def build_asan(verbose: bool = False) -> str:
+    os.makedirs(os.path.dirname(ASAN_LIB), exist_ok=True)
     tmp = ASAN_LIB + ".tmp"
     cmd = ["g++", *ASAN_FLAGS, "-fsanitize=address,undefined", SRC, "-o", tmp]
     if verbose:
