@@ -23,7 +23,7 @@ import os
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen",
            "fa_bwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_fp8",
-           "fa_merge",
+           "fa_merge", "fa_fwd_splitkv_noalloc", "fa_noalloc_scratch_bytes",
            "fa_bwd_workspace_size", "fa_status_string", "FAError", "library_path",
            "load_library"]
 
@@ -70,6 +70,10 @@ def load_library():
     lib.fa_fwd_splitkv_workspace_size.restype = s
     lib.fa_fwd_splitkv.argtypes = [vp] * 6 + [i, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_noalloc_scratch_bytes.argtypes = []
+    lib.fa_noalloc_scratch_bytes.restype = s
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = i
     lib.fa_fwd_fp8.argtypes = [vp] * 5 + [i, i, i, i, f, f, f, f, i, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_merge.argtypes = [vp] * 5 + [i, i, i, i, i, vp]
@@ -328,4 +332,35 @@ def fa_fwd_splitkv(q, k, v, causal=False, softmax_scale=None, num_splits=0, work
                             int(num_splits), _stream(q.device))
     if rc != FA_OK:
         raise FAError("fa_fwd_splitkv", rc)
+    return o, lse
+
+
+def fa_noalloc_scratch_bytes() -> int:
+    return int(load_library().fa_noalloc_scratch_bytes())
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, causal=False, softmax_scale=None, num_splits=0, out=None,
+                           lse=None):
+    """fa_fwd_splitkv with its workspace in the library's scratch array (the library
+    allocates nothing; see include/fa.h). Outputs are allocated here unless passed in.
+    Returns (o [B,Nq,H,d], lse fp32 [B,H,Nq])."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Nq, H, d] and k, v [B, Nk, H, d]")
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    _check_tensor("q", q, q.shape, q.dtype, q.device)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, Nk, H, d), q.dtype, q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("out", o, q.shape, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, H, Nq), torch.float32, q.device)
+    rc = lib.fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), B, Nq, Nk, H, d, _dtype_code(q),
+                                    _scale(softmax_scale, d), int(bool(causal)),
+                                    int(num_splits), _stream(q.device))
+    if rc != FA_OK:
+        raise FAError("fa_fwd_splitkv_noalloc", rc)
     return o, lse

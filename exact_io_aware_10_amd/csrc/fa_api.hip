@@ -315,16 +315,23 @@ FA_EXPORT size_t fa_fwd_splitkv_workspace_size(int B, int Nq, int Nk, int H, int
   return (size_t)rows * (d + 2) * 4;
 }
 
-FA_EXPORT fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
-                                   float* lse, void* workspace, int B, int Nq, int Nk, int H,
-                                   int d, int dtype, float softmax_scale, int causal,
-                                   int num_splits, hipStream_t stream) {
+namespace {
+
+// The checks and the launch of fa_fwd_splitkv; workspace is resolved by get_ws only after
+// every argument check has passed.
+template <class GetWs>
+fa_status splitkv_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                       GetWs get_ws, int B, int Nq, int Nk, int H, int d, int dtype,
+                       float softmax_scale, int causal, int num_splits, hipStream_t stream) {
   fa_status st = splitkv_sizes(B, Nq, Nk, H, d, num_splits);
   if (st != FA_OK) return st;
   if (!dtype_ok(dtype) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
   if ((long)B * Nq * H == 0) return FA_OK;
-  if (!tensors_ok({q, k, v, o, workspace}) || lse == nullptr || ((uintptr_t)lse & 3u))
+  if (!tensors_ok({q, k, v, o}) || lse == nullptr || ((uintptr_t)lse & 3u))
     return FA_ERR_INVALID_ARG;
+  void* workspace = nullptr;
+  if ((st = get_ws(&workspace)) != FA_OK) return st;
+  if (!tensors_ok({workspace})) return FA_ERR_INVALID_ARG;
   fa::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -344,4 +351,35 @@ FA_EXPORT fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, 
   a.scale_log2 = exp_scale(softmax_scale);
   a.qsign = softmax_scale < 0.f ? 0x80008000u : 0u;
   return to_status(fa::launch_decode(a, d, dtype == FA_BF16, causal != 0, stream));
+}
+
+}  // namespace
+
+FA_EXPORT fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, void* workspace, int B, int Nq, int Nk, int H,
+                                   int d, int dtype, float softmax_scale, int causal,
+                                   int num_splits, hipStream_t stream) {
+  auto ws = [workspace](void** out) {
+    *out = workspace;
+    return FA_OK;
+  };
+  return splitkv_impl(q, k, v, o, lse, ws, B, Nq, Nk, H, d, dtype, softmax_scale, causal,
+                      num_splits, stream);
+}
+
+FA_EXPORT size_t fa_noalloc_scratch_bytes(void) { return fa::kScratchBytes; }
+
+FA_EXPORT fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                           float* lse, int B, int Nq, int Nk, int H, int d,
+                                           int dtype, float softmax_scale, int causal,
+                                           int num_splits, hipStream_t stream) {
+  auto ws = [=](void** out) {
+    // the partials must fit the library's scratch array (this check follows the argument
+    // checks, so the size is well defined here)
+    if (fa_fwd_splitkv_workspace_size(B, Nq, Nk, H, d, num_splits) > fa::kScratchBytes)
+      return FA_ERR_UNSUPPORTED;
+    return fa::scratch_buffer(out) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  };
+  return splitkv_impl(q, k, v, o, lse, ws, B, Nq, Nk, H, d, dtype, softmax_scale, causal,
+                      num_splits, stream);
 }

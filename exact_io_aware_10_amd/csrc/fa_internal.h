@@ -93,4 +93,9 @@ __attribute__((visibility("hidden"))) hipError_t launch_bwd(const BwdArgs& a, in
                                                             bool causal, bool varlen, int stage,
                                                             hipStream_t stream);
 
+// Scratch array of the allocation-free entry points (fa_scratch.hip): its size, and the
+// device address of the current device's copy (looked up on the first call per device).
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+__attribute__((visibility("hidden"))) hipError_t scratch_buffer(void** out);
+
 }  // namespace fa

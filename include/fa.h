@@ -241,6 +241,27 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
                          void* workspace, int B, int Nq, int Nk, int H, int d, int dtype,
                          float softmax_scale, int causal, int num_splits, hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): fa_fwd_splitkv with its workspace in the
+ * library's own scratch array instead of a workspace argument. Same arguments, results and
+ * errors as fa_fwd_splitkv otherwise; the caller still passes q, k, v, o and lse.
+ *   - The scratch array is a static device array of fa_noalloc_scratch_bytes() bytes
+ *     (8 MiB), one copy per GPU, held until the process ends. A request whose
+ *     fa_fwd_splitkv_workspace_size exceeds it returns FA_ERR_UNSUPPORTED before any launch.
+ *   - The first call on a device looks up that device's copy (hipGetSymbolAddress, with the
+ *     device current); a failure there returns FA_ERR_HIP. No call allocates or frees memory.
+ *   - Every call on one GPU uses the same array: calls that overlap in time on one GPU (on
+ *     different streams, or from several host threads) race on it and give undefined
+ *     results. Calls in order on one stream are safe. Nothing in the array needs clearing:
+ *     the first kernel writes every partial the second one reads.
+ */
+size_t fa_noalloc_scratch_bytes(void);
+fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int B, int Nq, int Nk, int H, int d, int dtype,
+                                 float softmax_scale, int causal, int num_splits,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

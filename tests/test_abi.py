@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_prep",
          "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_varlen", "fa_bwd_varlen",
-         "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_merge"])
+         "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_merge",
+         "fa_noalloc_scratch_bytes", "fa_fwd_splitkv_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -200,3 +201,24 @@ def test_merge_argument_checks(lib):
     assert call(d=96) == 2
     assert call(N=1 << 20, H=64, d=128) == 2
     assert call(out=None, B=0) == 0             # empty: nothing to do
+
+
+def test_splitkv_noalloc_argument_checks(lib):
+    """The allocation-free split-KV entry point checks its arguments like fa_fwd_splitkv,
+    before it touches any device; requests whose partials exceed the scratch array are
+    refused as unsupported."""
+    f = ctypes.c_float(0.1)
+    call = lambda q=FAKE, B=1, Nq=1, Nk=8, H=1, d=64, dt=1, splits=0: \
+        lib.fa_fwd_splitkv_noalloc(q, FAKE, FAKE, FAKE, FAKE, B, Nq, Nk, H, d, dt, f, 0,
+                                   splits, None)
+    lib.fa_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    assert lib.fa_noalloc_scratch_bytes() == 8 << 20
+    assert call(q=None) == 1
+    assert call(dt=5) == 1
+    assert call(Nk=0) == 1
+    assert call(d=96) == 2
+    assert call(B=0) == 0
+    # 16 heads x 4096 ranges x 130 fp32 values per partial row: 34 MB, beyond 8 MiB
+    lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    assert lib.fa_fwd_splitkv_workspace_size(1, 1, 500000, 16, 128, 4096) > 8 << 20
+    assert call(Nk=500000, H=16, d=128, splits=4096) == 2
