@@ -24,9 +24,14 @@ def round_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     """fp32 array -> uint16 bit patterns of bf16 or fp16, round to nearest even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     if dtype == "bf16":
-        u = x.view(np.uint32).astype(np.uint64)
-        lsb = (u >> 16) & 1
-        return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+        # in 32-bit words: u + 0x7FFF + lsb stays below 2^32 for every finite value and
+        # infinity (u <= 0xFF800000); NaN patterns are kept NaN
+        u = x.view(np.uint32)
+        r = ((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
+        nan = np.isnan(x)
+        if nan.any():
+            r[nan] = (u[nan] >> 16).astype(np.uint16) | np.uint16(0x40)
+        return r
     if dtype == "f16":
         return x.astype(np.float16).view(np.uint16)
     raise ValueError(f"unknown dtype {dtype!r}")

@@ -54,14 +54,15 @@ def f64_of(t, dtype):
     return oracle.widen(bits_of(t), dtype)
 
 
-def err_stats(got, ref):
+def err_stats(got, ref, diff=None):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    d = np.abs(got - ref)
-    fro = np.linalg.norm((got - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300)
-    return {"max_abs": float(d.max()) if d.size else 0.0,
-            "mean_abs": float(d.mean()) if d.size else 0.0,
-            "rel_fro": float(fro) if d.size else 0.0}
+    e = got - ref if diff is None else diff
+    if not e.size:
+        return {"max_abs": 0.0, "mean_abs": 0.0, "rel_fro": 0.0}
+    d = np.abs(e)
+    fro = np.linalg.norm(e.ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300)
+    return {"max_abs": float(d.max()), "mean_abs": float(d.mean()), "rel_fro": float(fro)}
 
 
 def assert_close(name, got, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS, rel_fro=REL_FRO,
@@ -70,14 +71,19 @@ def assert_close(name, got, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS, rel_fro=REL
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    s = err_stats(got, ref)
+    diff = got - ref
+    s = err_stats(got, ref, diff)
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    slack = rtol * np.abs(ref) + (ulps * half_ulp_bf16(ref) if ulps else 0.0)
-    excess = float(np.max(np.abs(got - ref) - slack)) if ref.size else 0.0
+    ad = np.abs(diff)
+    if rtol or ulps:
+        excess = float(np.max(ad - rtol * np.abs(ref) - ulps * half_ulp_bf16(ref))) \
+            if ref.size else 0.0
+    else:
+        excess = s["max_abs"]
     if not quiet:
         at = ""
         if ref.size:
-            w = np.unravel_index(int(np.argmax(np.abs(got - ref))), ref.shape)
+            w = np.unravel_index(int(np.argmax(ad)), ref.shape)
             at = (f" worst at {tuple(int(i) for i in w)} ref={float(ref[w]):.4f} "
                   f"half-ulp={float(half_ulp_bf16(ref[w])):.2e}")
         print(f"  {name}: max_abs={s['max_abs']:.3e} mean_abs={s['mean_abs']:.3e} "
