@@ -63,7 +63,8 @@ fa_status check_common(long B, long N, long H, int d, int dt, float scale) {
   if (!dtype_ok(dt) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if ((N + 256) * H * d >= kMaxSliceElems) return FA_ERR_UNSUPPORTED;
-  if (B * H * ((N + 127) / 128) >= (1L << 31)) return FA_ERR_UNSUPPORTED;
+  // workgroups of the largest launch (128-row blocks; packed launches round B·H up to 8)
+  if ((B * H + 7) / 8 * 8 * ((N + 127) / 128) >= (1L << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // with 16 workgroups per CU the tail is short, and going longest first across the heads of
   // an XCD (as dQ does) streamed eight heads' Q and dO through its L2 at once and was 2-4%
   // slower at N = 8192
-  decode_work(a, nkb, VARLEN, false, false, kb, h, bs);
+  if (!decode_work(a, nkb, VARLEN, false, false, kb, h, bs)) return;
   const SliceInfo si = slice_info(a, bs, h);
   const int L = si.L;
   const int k0 = kb * BKV;
@@ -226,7 +226,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 template <int D, class T, bool CAUSAL, bool VARLEN>
 hipError_t launch_t(const BwdArgs& a, hipStream_t st) {
-  const long nblk = (long)((a.N + 127) / 128) * a.H * a.B;
+  const int nkb = (a.N + 127) / 128;
+  const long nblk = VARLEN ? varlen_grid(nkb, a.H, a.B) : (long)nkb * a.H * a.B;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(512),
                      0, st, a);
   return hipGetLastError();

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   Lanes<D> ln(lane);
   const int nqb = (a.N + BQ - 1) / BQ;
   int qb, h, bs;
-  decode_work(a, nqb, VARLEN, CAUSAL, true, qb, h, bs);
+  if (!decode_work(a, nqb, VARLEN, CAUSAL, true, qb, h, bs)) return;
   const SliceInfo si = slice_info(a, bs, h);
   const int L = si.L;
   const int q0 = qb * BQ;
@@ -161,7 +161,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 template <int D, class T, bool CAUSAL, bool VARLEN>
 hipError_t launch_t(const BwdArgs& a, hipStream_t st) {
   constexpr int BQ = 32 * kDqWaves;
-  const long nblk = (long)((a.N + BQ - 1) / BQ) * a.H * a.B;
+  const int nqb = (a.N + BQ - 1) / BQ;
+  const long nblk = VARLEN ? varlen_grid(nqb, a.H, a.B) : (long)nqb * a.H * a.B;
   hipLaunchKernelGGL((bwd_dq_kernel<D, T, CAUSAL, VARLEN>), dim3((unsigned)nblk),
                      dim3(kDqThreads), 0, st, a);
   return hipGetLastError();

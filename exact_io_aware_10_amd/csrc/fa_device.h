@@ -249,6 +249,28 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t lin, uint32_t total) {
   return x * q + (x < r ? x : r) + slot;
 }
 
+// Work order of packed (varlen) launches over (sequence, head, block) items. The pairs
+// p = s·H + h go to XCD p % 8, so every sequence's heads spread evenly over the XCDs, and each
+// XCD takes its pairs one after another, all nblk blocks of a pair in a row: its CUs work on
+// one head's keys and values at a time and share them in its L2 (dealing consecutive blocks of
+// a pair to different XCDs made every XCD fetch the same keys and values from memory). The
+// grid holds nblk slots for each of 8·ceil(H·nseq/8) pairs; slots past the last pair return
+// false. Blocks past a sequence's length are left to the caller (they exit at once).
+__device__ __forceinline__ bool varlen_order(uint32_t lin, int nblk, int H, int nseq, int& blk,
+                                             int& h, int& s) {
+  const uint32_t x = lin % 8, slot = lin / 8;
+  const uint32_t p = x + 8 * (slot / (uint32_t)nblk);
+  blk = (int)(slot % (uint32_t)nblk);
+  if (p >= (uint32_t)H * (uint32_t)nseq) return false;
+  h = (int)(p % (uint32_t)H);
+  s = (int)(p / (uint32_t)H);
+  return true;
+}
+// Grid size of a packed launch for varlen_order: nblk slots for each of 8·ceil(H·nseq/8) pairs.
+__host__ __device__ __forceinline__ long varlen_grid(int nblk, int H, int nseq) {
+  return (long)nblk * 8 * (((long)H * nseq + 7) / 8);
+}
+
 // Work order for causal launches over items (bh, r) whose cost falls with the rank r (r = 0
 // is the longest). The hardware deals workgroups round-robin over the 8 XCDs and each XCD
 // starts its share in order; here XCD x keeps a contiguous range of whole (b, h) slices (their

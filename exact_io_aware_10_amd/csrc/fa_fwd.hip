@@ -147,13 +147,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     qb = nqb - 1 - rank;
     h = bh % a.H;
     bs = bh / a.H;
+  } else if (VARLEN) {  // each (sequence, head) on one XCD, longest rows first
+    if (!varlen_order(blockIdx.x, nqb, a.H, a.B, qb, h, bs)) return;
+    qb = nqb - 1 - qb;
   } else {
-    uint32_t w = blockIdx.x;
-    if (!VARLEN) w = xcd_remap(w, gridDim.x);
+    const uint32_t w = xcd_remap(blockIdx.x, gridDim.x);
     qb = w % nqb;
     h = (w / nqb) % a.H;
     bs = w / (nqb * a.H);
-    if (VARLEN) qb = nqb - 1 - qb;  // longest rows first
   }
 
   long tok0;
@@ -558,7 +559,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t st) {
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, VARLEN, false>), dim3((unsigned)total),
+  const long grid = VARLEN ? varlen_grid(nqb, a.H, a.B) : total;
+  hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, VARLEN, false>), dim3((unsigned)grid),
                      dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
