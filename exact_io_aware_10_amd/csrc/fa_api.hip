@@ -68,6 +68,9 @@ fa_status check_common(long B, long N, long H, int d, int dt, float scale) {
   return FA_OK;
 }
 
+// Dense calls index their row terms by token (B * N of them) in 32-bit ints.
+bool tokens_ok(long B, long N) { return B * N <= INT32_MAX; }
+
 bool tensors_ok(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if (p == nullptr || !aligned16(p)) return false;
@@ -91,6 +94,7 @@ FA_EXPORT fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
                            int causal, hipStream_t stream) {
   fa_status st = check_common(B, N, H, d, dtype, softmax_scale);
   if (st != FA_OK) return st;
+  if (!tokens_ok(B, N)) return FA_ERR_UNSUPPORTED;
   if ((long)B * N * H == 0) return FA_OK;
   if (!tensors_ok({q, k, v, o}) || lse == nullptr || ((uintptr_t)lse & 3u))
     return FA_ERR_INVALID_ARG;
@@ -175,6 +179,7 @@ fa_status bwd_common(const void* q, const void* k, const void* v, const void* o,
                      float softmax_scale, int causal, int stage, hipStream_t stream) {
   fa_status st = check_common(B, N, H, d, dtype, softmax_scale);
   if (st != FA_OK) return st;
+  if (!tokens_ok(B, N)) return FA_ERR_UNSUPPORTED;
   if ((long)B * N * H == 0) return FA_OK;
   if (!tensors_ok({q, k, v, o, dout, dq, dk, dv, workspace}) || lse == nullptr ||
       ((uintptr_t)lse & 3u))

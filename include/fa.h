@@ -67,7 +67,9 @@ const char* fa_status_string(int status);
  *   q, k, v : in,  [B, N, H, d], dtype
  *   o       : out, [B, N, H, d], dtype
  *   lse     : out, fp32 [B, H, N]
- * B, N, H >= 0 (B*N*H == 0 is a no-op returning FA_OK). Limit: (N + 256) * H * d < 2^30.
+ * B, N, H >= 0 (B*N*H == 0 is a no-op returning FA_OK). Limits (else FA_ERR_UNSUPPORTED):
+ * (N + 256) * H * d < 2^30 (row offsets of a slice fit in 31 bits), B * N < 2^31 tokens, and
+ * 8 * ceil(B * H / 8) * ceil(N / 128) < 2^31 (the workgroup count of the largest launch).
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int N, int H, int d, int dtype, float softmax_scale, int causal,
@@ -183,7 +185,8 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
  *                 cu[num_seqs] = total_tokens
  *   max_seqlen  : host-side upper bound on the sequence lengths (sizes the grid without a
  *                 device-to-host copy); lengths above it are not processed.
- * Limit: (max_seqlen + 256) * H * d < 2^30. Sequences longer than max_seqlen are treated
+ * Limits: (max_seqlen + 256) * H * d < 2^30 and 8 * ceil(num_seqs * H / 8) *
+ * ceil(max_seqlen / 128) < 2^31. Sequences longer than max_seqlen are treated
  * as truncated to max_seqlen tokens (their later rows are not written). A malformed cu_seqlens gives undefined results
  * (out-of-range rows are clamped by hardware bounds checks, never read or written outside
  * the packed tensors). With the environment variable FA_DEBUG set to anything but "" or

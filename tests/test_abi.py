@@ -64,6 +64,9 @@ def test_fwd_argument_checks(lib):
     assert call_fwd(lib, d=96) == 2
     assert call_fwd(lib, d=256) == 2
     assert call_fwd(lib, N=1 << 20, H=64, d=128) == 2   # N*H*d beyond the offset range
+    assert call_fwd(lib, B=1 << 19, N=1 << 12) == 2     # B*N tokens beyond 2^31 - 1
+    # 8 * ceil(B * H / 8) * ceil(N / 128) workgroups beyond 2^31 - 1, within the other limits
+    assert call_fwd(lib, B=20000, N=16000, H=1024) == 2
     assert call_fwd(lib, B=0) == 0                    # empty problem: nothing to do
     assert call_fwd(lib, q=None, N=0) == 0
 
@@ -79,6 +82,7 @@ def test_bwd_argument_checks(lib):
     assert lib.fa_bwd(*bad, 1, 8, 1, 64, 1, f, 0, None) == 1
     assert lib.fa_bwd(*args, 1, 8, 1, 80, 1, f, 0, None) == 2
     assert lib.fa_bwd(*args, 0, 8, 1, 64, 1, f, 0, None) == 0
+    assert lib.fa_bwd(*args, 1 << 19, 1 << 12, 1, 64, 1, f, 0, None) == 2  # B*N > 2^31 - 1
     for stage in (lib.fa_bwd_prep, lib.fa_bwd_dkdv, lib.fa_bwd_dq):
         assert stage(*bad, 1, 8, 1, 64, 1, f, 0, None) == 1
         assert stage(*args, 1, 8, 1, 80, 1, f, 0, None) == 2
@@ -91,6 +95,9 @@ def test_varlen_argument_checks(lib):
     assert lib.fa_fwd_varlen(*a, FAKE, -1, 100, 64, 2, 64, 1, f, 1, None) == 1
     assert lib.fa_fwd_varlen(*a, FAKE, 2, 100, 64, 2, 72, 1, f, 1, None) == 2
     assert lib.fa_fwd_varlen(*a, FAKE, 2, 0, 64, 2, 64, 1, f, 1, None) == 0
+    # workgroups of the packed launch, 8 * ceil(num_seqs * H / 8) * ceil(max_seqlen / 128),
+    # beyond 2^31 - 1
+    assert lib.fa_fwd_varlen(*a, FAKE, 17000, 100, 16000, 1024, 64, 1, f, 1, None) == 2
 
 
 def test_workspace_is_linear_in_sequence_length(lib):
