@@ -290,8 +290,11 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a) {
   const int rg = lane / CPR, c = lane % CPR;
   const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= (long)a.B * a.H * a.S) return;
-  const int s = (int)(w % a.S);
-  const int h = (int)((w / a.S) % a.H);
+  // head-major: the four waves of a workgroup take four heads of one key range, so that
+  // together they read adjacent 256-byte pieces of each token's K and V rows (2.4% faster
+  // at B1 H16 Nk 131072 d128 than four ranges of one head)
+  const int h = (int)(w % a.H);
+  const int s = (int)((w / a.H) % a.S);
   const int b = (int)(w / ((long)a.S * a.H));
   const int j0 = min(s * a.span, a.Nk);
   const int j1 = min(j0 + a.span, a.Nk);
