@@ -134,6 +134,23 @@ def test_bwd_varlen_small(d, causal):
         assert_close(name, g, r, ulps=1)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen_many(d, causal):
+    """Many packed sequences of mixed lengths (one to five 128-key blocks) over five heads:
+    the (sequence, head) pairs do not fill whole rounds of eight, so the last round of the
+    packed work order has empty slots in both gradient kernels."""
+    lens = inputs.varlen_lengths(6000, 17, 600, seed=7)
+    assert (len(lens) * 5) % 8 != 0
+    cu, bits, got = run_varlen_bwd(lens, 5, d, "bf16", causal, seed=23)
+    q, k, v, do = (oracle.widen(x, "bf16") for x in bits)
+    scale = 1 / math.sqrt(d)
+    o, lse = oracle.fwd_varlen(q, k, v, cu, scale, causal)
+    ref = oracle.bwd_varlen(q, k, v, o, lse, do, cu, scale, causal)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert_close(name, g, r)
+
+
 def test_bwd_varlen_workload():
     """The packed causal workload (T = 131072, H16, d128) through forward and backward; the
     oracle recomputes every sequence on two heads (the first and the last) as complete

@@ -133,6 +133,21 @@ def test_fwd_varlen_small(d, causal):
     assert_close("LSE", lse, rlse)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_varlen_many(d, causal):
+    """Many packed sequences of mixed lengths (one to three 256-row query blocks) over five
+    heads: the (sequence, head) pairs do not fill whole rounds of eight, so the last round
+    of the packed work order has empty slots."""
+    lens = inputs.varlen_lengths(6000, 17, 600, seed=7)
+    assert (len(lens) * 5) % 8 != 0
+    cu, (qb, kb, vb), o, lse = run_varlen(lens, 5, d, "bf16", causal, seed=13)
+    w = lambda x: oracle.widen(x, "bf16")
+    ro, rlse = oracle.fwd_varlen(w(qb), w(kb), w(vb), cu, 1 / math.sqrt(d), causal)
+    assert_close("O", o, ro)
+    assert_close("LSE", lse, rlse)
+
+
 def test_fwd_varlen_workload():
     """The packed causal workload (T = 131072, H16, d128): every (sequence, head) pair
     against the oracle, and the tolerances per sequence."""
