@@ -186,10 +186,10 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
  *   max_seqlen  : host-side upper bound on the sequence lengths (sizes the grid without a
  *                 device-to-host copy); lengths above it are not processed.
  * Limits: (max_seqlen + 256) * H * d < 2^30 and 8 * ceil(num_seqs * H / 8) *
- * ceil(max_seqlen / 128) < 2^31. Sequences longer than max_seqlen are treated
- * as truncated to max_seqlen tokens (their later rows are not written). A malformed cu_seqlens gives undefined results
- * (out-of-range rows are clamped by hardware bounds checks, never read or written outside
- * the packed tensors). With the environment variable FA_DEBUG set to anything but "" or
+ * ceil(max_seqlen / 128) < 2^31. Sequences longer than max_seqlen are treated as truncated
+ * to max_seqlen tokens (their later rows are not written). A malformed cu_seqlens gives
+ * undefined results (out-of-range rows are clamped by hardware bounds checks, never read or
+ * written outside the packed tensors). With the environment variable FA_DEBUG set to anything but "" or
  * "0" (read at every call), the call first copies cu_seqlens to the host on `stream`,
  * waits for the stream, and returns FA_ERR_INVALID_ARG without launching anything if
  * cu[0] != 0, cu decreases anywhere or cu[num_seqs] != total_tokens (or the copy fails).

@@ -151,6 +151,38 @@ def test_bwd_varlen_many(d, causal):
         assert_close(name, g, r)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_max_seqlen_truncates(causal):
+    """A sequence longer than max_seqlen is processed as its first max_seqlen tokens, in the
+    forward and in both gradient kernels, and the other sequences are unaffected: each
+    sequence's first min(L, max_seqlen) rows of O, LSE, dQ, dK and dV against the oracle on
+    that many tokens alone."""
+    import torch
+    lens, mx, H, d, dt = [100, 700, 40, 301], 300, 2, 64, "bf16"
+    cu = inputs.cu_seqlens(lens)
+    T = int(cu[-1])
+    print(f"[varlen truncation] lens={lens} max_seqlen={mx} causal={causal}", flush=True)
+    bits = [inputs.normal_bits((T, H, d), dt, 31 + i) for i in range(4)]
+    q, k, v, do = (to_device(x, dt) for x in bits)
+    cu_d = torch.from_numpy(cu).cuda()
+    o, lse = fa().fa_fwd_varlen(q, k, v, cu_d, mx, causal=causal)
+    dq, dk, dv = fa().fa_bwd_varlen(q, k, v, o, lse, do, cu_d, mx, causal=causal)
+    torch.cuda.synchronize()
+    got = [f64_of(t, dt) for t in (o, dq, dk, dv)]
+    lse = lse.cpu().numpy().astype(np.float64)
+    w = [oracle.widen(x, dt) for x in bits]
+    scale = 1 / math.sqrt(d)
+    for s, L in enumerate(lens):
+        a, n = int(cu[s]), min(L, mx)
+        sq, sk, sv, sdo = (x[a:a + n][None] for x in w)
+        ro, rlse = oracle.fwd(sq, sk, sv, scale, causal)
+        ref = oracle.bwd(sq, sk, sv, ro, rlse, sdo, scale, causal)
+        assert_close(f"O seq {s}", got[0][a:a + n], ro[0])
+        assert_close(f"LSE seq {s}", lse[:, a:a + n], rlse[0])
+        for name, g, r in zip(("dQ", "dK", "dV"), got[1:], ref):
+            assert_close(f"{name} seq {s}", g[a:a + n], r[0])
+
+
 def test_bwd_varlen_workload():
     """The packed causal workload (T = 131072, H16, d128) through forward and backward; the
     oracle recomputes every sequence on two heads (the first and the last) as complete
