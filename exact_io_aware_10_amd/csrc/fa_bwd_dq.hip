@@ -91,11 +91,15 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         f32x16 s = f32x16{}, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) dp[r] = ndq;
+        // the products run at raised wave priority, so that a wave ready to issue one wins
+        // the SIMD's issue slot over the other wave's exponentials (0.9% faster at N = 8192)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
           s = mfma32<T>(ln.row_frag(ks, kb * 32, dc), qreg[dc], s);
           dp = mfma32<T>(ln.row_frag(vs, kb * 32, dc), doreg[dc], dp);
         }
+        __builtin_amdgcn_s_setprio(0);
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[r] = exp2f_hw(fmaf(s[r], c2, nlq));
@@ -105,6 +109,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
           for (int r = 0; r < 16; ++r)
             if (kt0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) > qi) p[r] = 0.f;
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           float ds[8];
@@ -117,6 +122,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
           for (int db = 0; db < DB; ++db)
             dqacc[db] = mfma32<T>(ln.tr_frag(ks, kc * 16, db), sf, dqacc[db]);
         }
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
