@@ -38,8 +38,8 @@ CFLAGS = [
 
 # Per-file flags. The dQ kernel's softmax-side VALU work reads the S and dP accumulators
 # directly, so its MFMA results are kept in VGPRs (in AGPRs they would be copied back for
-# every tile); the dK/dV kernel keeps the default (its 128 gradient accumulators live in
-# AGPRs).
+# every tile); the dK/dV kernel needs no flag (at 256 registers per wave the compiler
+# already keeps all its accumulators in VGPRs).
 # The forward kernel's row max reads MFMA results; without NaN semantics fmaxf needs no
 # canonicalizing instruction per input (NaN inputs still propagate through exp and the sums).
 FILE_FLAGS = {
