@@ -183,6 +183,44 @@ def test_varlen_max_seqlen_truncates(causal):
             assert_close(f"{name} seq {s}", g[a:a + n], r[0])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_stages_match_fa_bwd(causal):
+    """The three stages that fa_bwd runs, called one by one through their own entry points
+    with one workspace (row terms, then dK/dV, then dQ; the order a caller may change between
+    the last two), give fa_bwd's gradients bit for bit, and each stage writes only its own
+    outputs: gradient buffers a stage does not own keep a planted bit pattern."""
+    import torch
+    m = fa()
+    B, N, H, d, dt = 2, 700, 3, 128, "bf16"
+    print(f"[bwd stages] B={B} N={N} H={H} d={d} causal={causal}", flush=True)
+    bits = inputs.attention_inputs(B, N, H, d, dt, 61, with_dout=True)
+    q, k, v, do = (to_device(x, dt) for x in bits)
+    o, lse = m.fa_fwd(q, k, v, causal=causal)
+    ref = m.fa_bwd(q, k, v, o, lse, do, causal=causal)
+    ws = torch.empty(max(m.fa_bwd_workspace_size(B, N, H, d), 16), dtype=torch.uint8,
+                     device=q.device)
+    fill = lambda: torch.full_like(q, 0).view(torch.int16).fill_(0x7fc1).view(q.dtype)
+    for order in ("dkdv_first", "dq_first"):
+        grads = (fill(), fill(), fill())
+        m.fa_bwd_prep(q, k, v, o, lse, do, causal=causal, workspace=ws, grads=grads)
+        torch.cuda.synchronize()
+        for g in grads:  # the row terms go to the workspace only
+            assert torch.all(g.view(torch.int16) == 0x7fc1)
+        stages = [(m.fa_bwd_dkdv, (1, 2)), (m.fa_bwd_dq, (0,))]
+        if order == "dq_first":
+            stages.reverse()
+        written = set()
+        for stage, own in stages:
+            stage(q, k, v, o, lse, do, causal=causal, workspace=ws, grads=grads)
+            torch.cuda.synchronize()
+            written.update(own)
+            for i, g in enumerate(grads):
+                if i not in written:
+                    assert torch.all(g.view(torch.int16) == 0x7fc1), (order, i)
+        for i, (g, r) in enumerate(zip(grads, ref)):
+            assert torch.equal(g.view(torch.int16), r.view(torch.int16)), (order, i)
+
+
 def test_bwd_varlen_workload():
     """The packed causal workload (T = 131072, H16, d128) through forward and backward; the
     oracle recomputes every sequence on two heads (the first and the last) as complete
