@@ -307,6 +307,11 @@ fa_status splitkv_sizes(long B, long Nq, long Nk, long H, int d, int num_splits)
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if ((Nk + 256) * H * d >= kMaxSliceElems || (Nq + 256) * H * d >= kMaxSliceElems)
     return FA_ERR_UNSUPPORTED;
+  // workgroups of the launches: at most B·H·S·ceil(Nq / 32) for the partials (S key ranges)
+  // and B·H·Nq for the merge, each below 2^31
+  const long S = fa::decode_splits((int)B, (int)Nq, (int)Nk, (int)H, d, num_splits);
+  if (B * H * S * ((Nq + 31) / 32) >= (1L << 31) || B * H * Nq >= (1L << 31))
+    return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

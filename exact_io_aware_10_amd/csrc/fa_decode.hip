@@ -501,6 +501,7 @@ hipError_t launch_c(const DecodeArgs& a, bool causal, hipStream_t st) {
 
 int decode_splits(int B, int Nq, int Nk, int H, int d, int requested) {
   const long tiles = (Nk + dec::kTK - 1) / dec::kTK;  // at least one tile per range
+  if ((long)B * H * Nq <= 0 || tiles <= 0) return 1;   // nothing to split
   long s = requested;
   if (s <= 0 && Nq == 1) {
     // single-row kernel: about one wave per SIMD of a 256-CU part, each streaming a long

@@ -236,7 +236,8 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  *                (none when Nk - Nq + i < 0: such rows get O = 0 and lse = -inf). With
  *                Nq = Nk this is fa_fwd's causal mask.
  * B, Nq, H >= 0 (B*Nq*H == 0 is a no-op returning FA_OK); Nk >= 1.
- * Limits: (Nk + 256) * H * d < 2^30 and (Nq + 256) * H * d < 2^30.
+ * Limits: (Nk + 256) * H * d < 2^30, (Nq + 256) * H * d < 2^30, B * H * S * ceil(Nq / 32)
+ * < 2^31 (S the number of key ranges used) and B * H * Nq < 2^31.
  * Deterministic: a fixed num_splits gives identical bits on every call.
  */
 size_t fa_fwd_splitkv_workspace_size(int B, int Nq, int Nk, int H, int d, int num_splits);

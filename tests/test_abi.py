@@ -146,6 +146,8 @@ def test_splitkv_argument_checks(lib):
     assert call(1, 1, 64, 2, 64, 1, 0, 0, scale=ctypes.c_float(float("nan"))) == 1
     assert call(1, 1, 64, 2, 72, 1, 0, 0) == 2       # head dim
     assert call(1, 1, 1 << 24, 2, 128, 1, 0, 0) == 2  # key rows beyond the offset range
+    # workgroups of the partials, B * H * S * ceil(Nq / 32), beyond 2^31 - 1
+    assert call(1 << 20, 1, 1 << 17, 16, 64, 1, 0, 4096) == 2
     misaligned = list(a)
     misaligned[0] = FAKE + 2
     assert call(1, 1, 64, 2, 64, 1, 0, 0, ptrs=misaligned) == 1
@@ -168,6 +170,9 @@ def test_splitkv_workspace_size(lib):
     auto = ws(4, 1, 8192, 16, 128, 0)
     assert auto > 0 and auto % (4 * 16 * (128 + 2) * 4) == 0
     assert ws(1, 1, 64, 1, 96, 0) == 0 and ws(-1, 1, 64, 1, 64, 0) == 0
+    # empty problems need no workspace (and the range count of an empty problem is defined)
+    assert ws(0, 1, 64, 2, 64, 0) == 0 and ws(1, 0, 64, 2, 64, 0) == 0
+    assert ws(1, 1, 64, 0, 64, 0) == 0
 
 
 def test_fp8_argument_checks(lib):
