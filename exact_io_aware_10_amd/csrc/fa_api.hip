@@ -149,6 +149,8 @@ FA_EXPORT fa_status fa_merge(float* o_acc, float* lse_acc, const void* o_part,
                              int dtype, hipStream_t stream) {
   fa_status st = check_common(B, N, H, d, dtype, 1.0f);
   if (st != FA_OK) return st;
+  // workgroups of the merge: B·N·H rows, at least 8 per workgroup, below 2^31
+  if ((long)B * N * H >= (1L << 34)) return FA_ERR_UNSUPPORTED;
   if ((long)B * N * H == 0) return FA_OK;
   if (!tensors_ok({o_acc, o_part}) || (out != nullptr && !aligned16(out)) ||
       lse_acc == nullptr || lse_part == nullptr || ((uintptr_t)lse_acc & 3u) ||

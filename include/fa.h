@@ -116,8 +116,8 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
  *   o_part   : in, [B, N, H, d], dtype
  *   lse_part : in, fp32 [B, H, N]
  *   out      : out, [B, N, H, d], dtype, or NULL: the merged output rounded to dtype
- * dtype FA_BF16 or FA_F16, d 64 or 128, sizes and limits as fa_fwd. Deterministic. For the
- * backward, fa_bwd on each shard with the merged o (rounded) and lse gives that shard's dK,
+ * dtype FA_BF16 or FA_F16, d 64 or 128, sizes and limits as fa_fwd (B * N tokens aside),
+ * and B * N * H < 2^34. Deterministic. For the backward, fa_bwd on each shard with the merged o (rounded) and lse gives that shard's dK,
  * dV and its share of dQ (the shares of dQ add up).
  */
 fa_status fa_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part,

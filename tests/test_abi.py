@@ -212,6 +212,7 @@ def test_merge_argument_checks(lib):
     assert call(dt=5) == 1
     assert call(d=96) == 2
     assert call(N=1 << 20, H=64, d=128) == 2
+    assert call(B=1 << 22, N=1 << 12) == 2      # workgroups beyond 2^31 - 1
     assert call(out=None, B=0) == 0             # empty: nothing to do
 
 
