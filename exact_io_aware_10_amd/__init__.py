@@ -17,6 +17,7 @@ lse: fp32 [B, H, N] (packed: [H, T]); d in {64, 128}; softmax_scale defaults to 
 fa_fwd_fp8 takes e4m3 tensors (torch.float8_e4m3fn, or uint8 holding the codes) with one
 float descale per tensor and returns a bf16 output.
 """
+import contextlib
 import ctypes
 import math
 import os
@@ -121,6 +122,15 @@ def _stream(device):
     return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
 
 
+def _on(device):
+    """Context in which the library's kernels go to `device` (the library launches on the
+    current HIP device): a no-op when that is already the current one."""
+    torch = _torch()
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
 def _scale(softmax_scale, d):
     return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
 
@@ -138,9 +148,10 @@ def fa_fwd(q, k, v, causal=False, softmax_scale=None, out=None, lse=None):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor("out", o, q.shape, q.dtype, q.device)
     _check_tensor("lse", lse, (B, H, N), torch.float32, q.device)
-    rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                    B, N, H, d, _dtype_code(q), _scale(softmax_scale, d), int(bool(causal)),
-                    _stream(q.device))
+    with _on(q.device):
+        rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, N, H, d, _dtype_code(q), _scale(softmax_scale, d), int(bool(causal)),
+                        _stream(q.device))
     if rc != FA_OK:
         raise FAError("fa_fwd", rc)
     return o, lse
@@ -164,9 +175,10 @@ def fa_fwd_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=Fals
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor("out", o, q.shape, torch.bfloat16, q.device)
     _check_tensor("lse", lse, (B, H, N), torch.float32, q.device)
-    rc = lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                        B, N, H, d, float(q_descale), float(k_descale), float(v_descale),
-                        _scale(softmax_scale, d), int(bool(causal)), _stream(q.device))
+    with _on(q.device):
+        rc = lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, N, H, d, float(q_descale), float(k_descale), float(v_descale),
+                            _scale(softmax_scale, d), int(bool(causal)), _stream(q.device))
     if rc != FA_OK:
         raise FAError("fa_fwd_fp8", rc)
     return o, lse
@@ -187,9 +199,10 @@ def fa_merge(o_acc, lse_acc, o_part, lse_part, out=None):
     _check_tensor("lse_part", lse_part, (B, H, N), torch.float32, o_part.device)
     if out is not None:
         _check_tensor("out", out, o_part.shape, o_part.dtype, o_part.device)
-    rc = lib.fa_merge(o_acc.data_ptr(), lse_acc.data_ptr(), o_part.data_ptr(),
-                      lse_part.data_ptr(), None if out is None else out.data_ptr(), B, N, H, d,
-                      _dtype_code(o_part), _stream(o_part.device))
+    with _on(o_part.device):
+        rc = lib.fa_merge(o_acc.data_ptr(), lse_acc.data_ptr(), o_part.data_ptr(),
+                          lse_part.data_ptr(), None if out is None else out.data_ptr(), B, N, H, d,
+                          _dtype_code(o_part), _stream(o_part.device))
     if rc != FA_OK:
         raise FAError("fa_merge", rc)
     return out
@@ -212,10 +225,11 @@ def _bwd_call(fn, q, k, v, o, lse, dout, causal, softmax_scale, workspace, grads
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
     dq, dk, dv = grads
-    rc = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                          lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                          dv.data_ptr(), workspace.data_ptr(), B, N, H, d, _dtype_code(q),
-                          _scale(softmax_scale, d), int(bool(causal)), _stream(q.device))
+    with _on(q.device):
+        rc = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), workspace.data_ptr(), B, N, H, d, _dtype_code(q),
+                              _scale(softmax_scale, d), int(bool(causal)), _stream(q.device))
     if rc != FA_OK:
         raise FAError(fn, rc)
     return grads
@@ -264,10 +278,11 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, softmax_scale=N
         raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
     o = torch.empty_like(q)
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    rc = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                           lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T,
-                           int(max_seqlen), H, d, _dtype_code(q), _scale(softmax_scale, d),
-                           int(bool(causal)), _stream(q.device))
+    with _on(q.device):
+        rc = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, T,
+                               int(max_seqlen), H, d, _dtype_code(q), _scale(softmax_scale, d),
+                               int(bool(causal)), _stream(q.device))
     if rc != FA_OK:
         raise FAError("fa_fwd_varlen", rc)
     return o, lse
@@ -291,11 +306,12 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, causal=False,
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
-    rc = lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                           lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                           dv.data_ptr(), workspace.data_ptr(), cu_seqlens.data_ptr(),
-                           cu_seqlens.numel() - 1, T, int(max_seqlen), H, d, _dtype_code(q),
-                           _scale(softmax_scale, d), int(bool(causal)), _stream(q.device))
+    with _on(q.device):
+        rc = lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), workspace.data_ptr(), cu_seqlens.data_ptr(),
+                               cu_seqlens.numel() - 1, T, int(max_seqlen), H, d, _dtype_code(q),
+                               _scale(softmax_scale, d), int(bool(causal)), _stream(q.device))
     if rc != FA_OK:
         raise FAError("fa_bwd_varlen", rc)
     return dq, dk, dv
@@ -326,10 +342,11 @@ def fa_fwd_splitkv(q, k, v, causal=False, softmax_scale=None, num_splits=0, work
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
-    rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                            lse.data_ptr(), workspace.data_ptr(), B, Nq, Nk, H, d,
-                            _dtype_code(q), _scale(softmax_scale, d), int(bool(causal)),
-                            int(num_splits), _stream(q.device))
+    with _on(q.device):
+        rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), workspace.data_ptr(), B, Nq, Nk, H, d,
+                                _dtype_code(q), _scale(softmax_scale, d), int(bool(causal)),
+                                int(num_splits), _stream(q.device))
     if rc != FA_OK:
         raise FAError("fa_fwd_splitkv", rc)
     return o, lse
@@ -357,10 +374,11 @@ def fa_fwd_splitkv_noalloc(q, k, v, causal=False, softmax_scale=None, num_splits
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor("out", o, q.shape, q.dtype, q.device)
     _check_tensor("lse", lse, (B, H, Nq), torch.float32, q.device)
-    rc = lib.fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                    lse.data_ptr(), B, Nq, Nk, H, d, _dtype_code(q),
-                                    _scale(softmax_scale, d), int(bool(causal)),
-                                    int(num_splits), _stream(q.device))
+    with _on(q.device):
+        rc = lib.fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        lse.data_ptr(), B, Nq, Nk, H, d, _dtype_code(q),
+                                        _scale(softmax_scale, d), int(bool(causal)),
+                                        int(num_splits), _stream(q.device))
     if rc != FA_OK:
         raise FAError("fa_fwd_splitkv_noalloc", rc)
     return o, lse
