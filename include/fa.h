@@ -16,8 +16,9 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller. The library allocates
  *    nothing, keeps no global state, never synchronises, and enqueues its kernels on
- *    `stream` (a hipStream_t; NULL means the default stream). Calls on different streams
- *    may run concurrently.
+ *    `stream` (a hipStream_t; NULL means the default stream). Kernels are launched on the
+ *    calling thread's current HIP device, to which the tensors and the stream must belong.
+ *    Calls on different streams may run concurrently.
  *  - Layout: q, k, v, o, dout, dq, dk, dv are [B, N, H, d] row-major (d contiguous, then
  *    heads, then tokens, then batch), 16-byte aligned. lse is fp32 [B, H, N].
  *    Packed (varlen) tensors are [T, H, d] with lse fp32 [H, T].
