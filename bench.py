@@ -12,7 +12,7 @@ forward-only rate, each kernel's live HIP-event timing, the roofline of the domi
 kernel against MI355X's dense bf16 MFMA peak, and the fp64 CPU oracle timed on a bounded
 sample of the same workload (the CPU baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-clock]
        python bench.py --copy-calibration MIB ...   also runs one plain device-to-device
                                                      copy of MIB MiB before the timed
                                                      region (reference kernel for the HBM
@@ -48,6 +48,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak (vendor figure, no sparsity)
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA peak (vendor figure, no sparsity)
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E peak bandwidth (vendor figure)
+BF16_FLOP_PER_CLK_CU = 4096  # dense bf16 MFMA FLOP per clock per CU (4 SIMDs)
 CSRC = os.path.join(ROOT, "exact_io_aware_10_amd", "csrc")
 KERNEL_SOURCES = {  # the files whose text determines each kernel's code (build.py: flags)
     "decode_kernel": ["fa_decode.hip", "fa_decode.h", "fa_bwd_common.h", "fa_device.h",
@@ -85,6 +86,62 @@ def host_cores():
     except AttributeError:  # pragma: no cover
         aff = os.cpu_count() or 1
     return oracle.default_threads(), aff, os.cpu_count() or aff
+
+
+def parse_sclk_mhz(text):
+    """Shader clock in MHz from the output of `rocm-smi --showgpuclocks [--json]`: the first
+    card's value of a key naming sclk ("(1640Mhz)", "1 (158Mhz)"), or None if there is none."""
+    import re
+    num = re.compile(r"(\d+(?:\.\d+)?)\s*mhz", re.I)
+    try:  # the JSON object may follow warning lines
+        data = json.loads(text[text.index("{"):])
+    except ValueError:
+        data = None
+    if isinstance(data, dict):
+        for card in sorted(data):
+            fields = data[card]
+            if not isinstance(fields, dict):
+                continue
+            for key, val in fields.items():
+                m = num.search(str(val)) if "sclk" in key.lower() else None
+                if m:
+                    return float(m.group(1))
+    for line in text.splitlines():
+        m = num.search(line) if "sclk" in line.lower() else None
+        if m:
+            return float(m.group(1))
+    return None
+
+
+def sustained_clock(step, seconds=2.0, limit_s=30.0):
+    """Runs `step` back to back for about `seconds` (at most `limit_s`) and reads the shader
+    clock with rocm-smi half-way through, from a second thread (a child process: this one
+    keeps the GPU busy). One reading at one moment of the step loop, whichever kernel runs
+    then. Returns MHz, or None where rocm-smi is missing or says nothing."""
+    import subprocess
+    import threading
+    import torch
+    got = {}
+
+    def probe():
+        time.sleep(seconds / 2)
+        try:
+            r = subprocess.run(["rocm-smi", "--showgpuclocks", "--json"], capture_output=True,
+                               text=True, timeout=20)
+            got["mhz"] = parse_sclk_mhz(r.stdout)
+        except (OSError, subprocess.SubprocessError):
+            got["mhz"] = None
+
+    th = threading.Thread(target=probe, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while (th.is_alive() or time.perf_counter() - t0 < seconds) and \
+            time.perf_counter() - t0 < limit_s:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    return got.get("mhz")
 
 
 def cpu_baseline(wl, bits, fwd_slices=16, bwd_slices=4):
@@ -645,6 +702,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the sustained-clock reading after the timed region")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--configs", action="store_true",
                     help="print a table of the five parity configurations (forward and "
@@ -787,6 +846,21 @@ def main():
         "wall_s": round(wall, 3),
         "roofline": roofline,
     }
+    if not args.no_clock:
+        # after the timed region: the chip runs these kernels below the 2.4 GHz that the
+        # vendor peak assumes (power-limited), so give the peak at the clock it sustained too
+        mhz = sustained_clock(step)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        clock = {"sclk_mhz": mhz, "cus": cus,
+                 "how": "rocm-smi --showgpuclocks, one reading half-way through 2 s of "
+                        "back-to-back steps after the timed region; bf16 peak at that clock = CUs x clock "
+                        "x 4096 FLOP (one 32x32x16 MFMA per SIMD per 32 cycles)"}
+        if mhz:
+            pk = cus * mhz * 1e6 * BF16_FLOP_PER_CLK_CU / 1e12
+            clock.update(bf16_peak_at_sclk=round(pk, 1),
+                         step_frac_at_sclk=round(tflops / pk, 4),
+                         fwd_frac_at_sclk=round(fwd_tflops / pk, 4))
+        out["clock"] = clock
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, bits)
     print(json.dumps(out), flush=True)
